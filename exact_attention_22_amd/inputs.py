@@ -1,0 +1,91 @@
+"""Seeded synthetic workloads for the attention forward.
+
+This module holds no attention arithmetic: it only names the workloads and draws
+their Q/K/V from a seeded normal generator.  Both sides of every parity check (the
+HIP library and the fp64 oracle) receive the exact same 16-bit patterns from here.
+
+Workloads (Q, K, V iid N(0, 1), layout [B, H, N, d], scale = 1/sqrt(d)):
+  tiny            B=1  H=1  Nq=Nk=128   d=64  fp16  non-causal
+  prefill_d64     B=16 H=16 Nq=Nk=1024  d=64  fp16  non-causal
+  causal_d128     B=4  H=16 Nq=Nk=2048  d=128 fp16  causal
+  long_causal     B=1  H=32 Nq=Nk=8192  d=128 bf16  causal, values scaled by 0.5
+  decode          B=8  H=32 Nq=1 Nk=32768 d=128 fp16 non-causal, 16 KV splits
+These follow the shapes the pages benchmark (randn fp16, d in {64, 128},
+N from 1K to 16K) -- no dataset is involved.
+"""
+from dataclasses import dataclass, replace
+import math
+
+import torch
+
+F16 = torch.float16
+BF16 = torch.bfloat16
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: torch.dtype
+    causal: bool
+    mult: float = 1.0        # the long-context workload draws N(0,1) * 0.5
+    splits: int = 0          # > 0: decode through split-KV + combine
+    seed: int = 42
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = [
+    Workload("tiny", 1, 1, 128, 128, 64, F16, False, seed=42),
+    Workload("prefill_d64", 16, 16, 1024, 1024, 64, F16, False, seed=43),
+    Workload("causal_d128", 4, 16, 2048, 2048, 128, F16, True, seed=44),
+    Workload("long_causal", 1, 32, 8192, 8192, 128, BF16, True, mult=0.5, seed=45),
+    Workload("decode", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=46),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def make_qkv(w: Workload, device="cpu"):
+    """Draw Q, then K, then V as float32 N(0,1) (times w.mult), cast to w.dtype.
+
+    The generator runs on `device`, so the bits depend on it; callers that need
+    the same data on the CPU copy the tensors rather than drawing again.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    out = []
+    for n in (w.Nq, w.Nk, w.Nk):
+        x = torch.randn((w.B, w.H, n, w.d), generator=g, dtype=torch.float32, device=device)
+        if w.mult != 1.0:
+            x.mul_(w.mult)
+        out.append(x.to(w.dtype))
+        del x
+    return tuple(out)
+
+
+def make_partials(S, B, H, Nq, d, seed=7, device="cpu", empty_every=0):
+    """Seeded fp32 partial results for exercising a split combine on its own.
+
+    o_part [S,B,H,Nq,d] ~ N(0,1); lse_part [S,B,H,Nq] ~ 4*N(0,1).  With
+    empty_every = k > 0, every k-th split of every row is marked empty (-inf).
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    o = torch.randn((S, B, H, Nq, d), generator=g, dtype=torch.float32, device=device)
+    lse = 4.0 * torch.randn((S, B, H, Nq), generator=g, dtype=torch.float32, device=device)
+    if empty_every > 0:
+        R = B * H * Nq
+        s_idx = torch.arange(S, device=device)[:, None]
+        r_idx = torch.arange(R, device=device)[None, :]
+        empty = ((s_idx + r_idx) % empty_every == 0).reshape(S, B, H, Nq)
+        lse[empty] = -math.inf
+    return o, lse

@@ -1,0 +1,225 @@
+/*
+ * oracle/attention.c -- fp64 CPU reference for the FlashAttention-2 forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it.  It shares no code, header or table with the HIP kernels.
+ *
+ * What it computes is the plain definition of attention, not the tiled method:
+ * FlashAttention is exact (it reaches the three-step result, up to summation
+ * order), so the reference is that result written out in double precision.
+ *
+ *   Sources (the four web pages this project is built from):
+ *   - Ringi, "Lecture 25: why attention need not store the intermediate matrix"
+ *     section 1.1 (S = QK^T, P = softmax(S), O = PV) and section 2.1 (safe softmax:
+ *     m = max x, l = sum e^{x-m}, p = e^{x-m}/l).
+ *   - AIInfraGuide 6.2 "FlashAttention V2 explained", section 5.1 (the causal mask
+ *     adds -inf before the softmax) and the forward pseudocode of section 6
+ *     (the saved statistic is L = m + log l).
+ *   - LLM Infra Atlas "FA2: parallelism and work partitioning", section 4 (the
+ *     causal key bound is offset by seqlen_k - seqlen_q, i.e. bottom-right
+ *     alignment when Nq != Nk).
+ *   - KingOfEgg, "Flash Attention (4): v2.1 forward vs official source", section 3.5
+ *     (lse = row_max * scale + log(sum); an empty row normalises to O = 0).
+ *
+ * For one (b, h, query i) and a key range [kb, ke):
+ *   visible  V_i = { j : kb <= j < ke, j < Nk, and (not causal or j <= i + Nk - Nq) }
+ *   s_ij     = sigma * sum_t q[i,t] k[j,t]         (sigma = the float scale, widened)
+ *   m_i      = max_{j in V_i} s_ij
+ *   l_i      = sum_{j in V_i} exp(s_ij - m_i)
+ *   O_i      = sum_{j in V_i} exp(s_ij - m_i) v_j / l_i
+ *   LSE_i    = m_i + ln l_i                         (natural log, scaled-score units)
+ *   V_i empty: O_i = 0 and LSE_i = -inf.
+ *
+ * Inputs are raw 16-bit patterns (IEEE binary16 or bfloat16) decoded here exactly.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <pthread.h>
+
+#define ORACLE_F16 0
+#define ORACLE_BF16 1
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_decode_f16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double mag;
+    if (expo == 0) {
+        mag = ldexp((double)frac, -24);               /* subnormal: frac * 2^-24 */
+    } else if (expo == 31) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/2^10) * 2^(e-15) */
+    }
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_decode_bf16(uint16_t b) {
+    int sign = (b >> 15) & 1;
+    int expo = (b >> 7) & 0xff;
+    int frac = b & 0x7f;
+    double mag;
+    if (expo == 0) {
+        mag = ldexp((double)frac, -133);              /* subnormal: frac * 2^-133 */
+    } else if (expo == 255) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(128 + frac), expo - 134); /* (1 + frac/2^7) * 2^(e-127) */
+    }
+    return sign ? -mag : mag;
+}
+
+static double decode(uint16_t x, int dtype) {
+    return dtype == ORACLE_BF16 ? oracle_decode_bf16(x) : oracle_decode_f16(x);
+}
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int dtype, B, H, Nq, Nk, d, causal;
+    double sigma;
+    int key_begin, key_end;
+    const int64_t *rows;      /* flat (b*H + h)*Nq + i indices, or NULL for all rows */
+    int64_t nrows;
+    double *o, *lse;          /* o: [nrows, d], lse: [nrows] */
+    int64_t first, last;      /* this worker's slice of [0, nrows) */
+} job_t;
+
+/* One query row, written straight from the definition above. */
+static void one_row(const job_t *jb, int64_t flat, double *o_row, double *lse_out,
+                    double *qrow, double *s) {
+    const int d = jb->d, Nq = jb->Nq, Nk = jb->Nk;
+    const int64_t bh = flat / Nq;
+    const int i = (int)(flat % Nq);
+    const uint16_t *qp = jb->q + ((size_t)bh * Nq + i) * d;
+    const uint16_t *kp = jb->k + (size_t)bh * Nk * d;
+    const uint16_t *vp = jb->v + (size_t)bh * Nk * d;
+
+    int lo = jb->key_begin < 0 ? 0 : jb->key_begin;
+    int hi = jb->key_end > Nk ? Nk : jb->key_end;
+    if (jb->causal) {
+        int64_t lim = (int64_t)i + (Nk - Nq) + 1;          /* keys j <= i + Nk - Nq */
+        if (lim < hi) hi = lim < lo ? lo : (int)lim;
+    }
+    for (int t = 0; t < d; ++t) o_row[t] = 0.0;
+    if (hi <= lo) { *lse_out = -INFINITY; return; }
+
+    for (int t = 0; t < d; ++t) qrow[t] = decode(qp[t], jb->dtype);
+
+    /* scores of the visible keys and their maximum */
+    double m = -INFINITY;
+    for (int j = lo; j < hi; ++j) {
+        double acc = 0.0;
+        const uint16_t *kj = kp + (size_t)j * d;
+        for (int t = 0; t < d; ++t) acc += qrow[t] * decode(kj[t], jb->dtype);
+        s[j - lo] = jb->sigma * acc;
+        if (s[j - lo] > m) m = s[j - lo];
+    }
+    /* softmax denominator and weighted sum of V */
+    double l = 0.0;
+    for (int j = lo; j < hi; ++j) {
+        double p = exp(s[j - lo] - m);
+        l += p;
+        const uint16_t *vj = vp + (size_t)j * d;
+        for (int t = 0; t < d; ++t) o_row[t] += p * decode(vj[t], jb->dtype);
+    }
+    for (int t = 0; t < d; ++t) o_row[t] /= l;
+    *lse_out = m + log(l);
+}
+
+static void *worker(void *arg) {
+    job_t *jb = (job_t *)arg;
+    double *qrow = (double *)malloc(sizeof(double) * (size_t)jb->d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
+    if (!qrow || !s) { free(qrow); free(s); return (void *)1; }
+    for (int64_t r = jb->first; r < jb->last; ++r) {
+        int64_t flat = jb->rows ? jb->rows[r] : r;
+        one_row(jb, flat, jb->o + r * jb->d, jb->lse + r, qrow, s);
+    }
+    free(qrow);
+    free(s);
+    return NULL;
+}
+
+/*
+ * Attention rows of [B, H, Nq, d] queries against [B, H, Nk, d] keys/values,
+ * restricted to keys in [key_begin, key_end).  rows == NULL means every row in
+ * flat order (nrows must then be B*H*Nq).  Returns 0, or -1 on a bad argument,
+ * -2 on allocation or thread failure.
+ */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
+                          int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                          int key_begin, int key_end, const int64_t *rows, int64_t nrows,
+                          double *o, double *lse, int nthreads) {
+    if (!q || !k || !v || !o || !lse) return -1;
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || nrows < 0) return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    const int64_t total = (int64_t)B * H * Nq;
+    if (!rows && nrows != total) return -1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= total) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+
+    job_t base = {q, k, v, dtype, B, H, Nq, Nk, d, causal, (double)scale,
+                  key_begin, key_end, rows, nrows, o, lse, 0, 0};
+    job_t jobs[256];
+    pthread_t tid[256];
+    int started[256];
+    int rc = 0;
+    for (int w = 0; w < nthreads; ++w) {
+        jobs[w] = base;
+        jobs[w].first = nrows * w / nthreads;
+        jobs[w].last = nrows * (w + 1) / nthreads;
+        started[w] = pthread_create(&tid[w], NULL, worker, &jobs[w]) == 0;
+        if (!started[w]) worker(&jobs[w]);   /* run inline if a thread cannot start */
+    }
+    for (int w = 0; w < nthreads; ++w) {
+        void *ret = NULL;
+        if (started[w]) pthread_join(tid[w], &ret);
+        if (ret) rc = -2;
+    }
+    return rc;
+}
+
+/*
+ * Merge of per-split partial results (split-KV decode).  The pages give only
+ * "each split emits a partial (O, LSE), a combine kernel merges them" (LLM Infra
+ * Atlas, "FA2: parallelism", section 2) together with the merge identity of the
+ * online softmax (Ringi, Lecture 25, section 2.2):
+ *   l_new = l_prev * e^{m_prev - m_new} + l_cur * e^{m_cur - m_new}.
+ * With normalised partials O_s and LSE_s = m_s + ln l_s this reads
+ *   M = max_s LSE_s;  w_s = e^{LSE_s - M} (0 when LSE_s = -inf);
+ *   O = sum_s w_s O_s / sum_s w_s;  LSE = M + ln sum_s w_s  (-inf if every split is empty).
+ * o_part: [S, R, d], lse_part: [S, R]; outputs o: [R, d], lse: [R].
+ */
+int oracle_combine(const double *o_part, const double *lse_part, int S, int64_t R, int d,
+                   double *o, double *lse) {
+    if (!o_part || !lse_part || !o || !lse || S <= 0 || R < 0 || d <= 0) return -1;
+    for (int64_t r = 0; r < R; ++r) {
+        double M = -INFINITY;
+        for (int s = 0; s < S; ++s)
+            if (lse_part[(size_t)s * R + r] > M) M = lse_part[(size_t)s * R + r];
+        double *orow = o + r * d;
+        for (int t = 0; t < d; ++t) orow[t] = 0.0;
+        if (M == -INFINITY) { lse[r] = -INFINITY; continue; }
+        double wsum = 0.0;
+        for (int s = 0; s < S; ++s) {
+            double ls = lse_part[(size_t)s * R + r];
+            if (ls == -INFINITY) continue;
+            double w = exp(ls - M);
+            wsum += w;
+            const double *op = o_part + ((size_t)s * R + r) * d;
+            for (int t = 0; t < d; ++t) orow[t] += w * op[t];
+        }
+        for (int t = 0; t < d; ++t) orow[t] /= wsum;
+        lse[r] = M + log(wsum);
+    }
+    return 0;
+}

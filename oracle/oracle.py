@@ -1,0 +1,150 @@
+"""Python access to the fp64 CPU oracle (oracle/attention.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg -- never by the product path.
+
+Every function follows the plain definition of attention documented at the top
+of attention.c (safe softmax of the scaled, masked scores; LSE = m + ln l; an
+empty row gives O = 0, LSE = -inf), evaluated in double precision.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(HERE, "liboracle.so")
+_DTYPE_CODE = {torch.float16: 0, torch.bfloat16: 1}
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def default_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _bits(t):
+    """Raw 16-bit patterns of a CPU fp16/bf16 tensor as a contiguous uint16 array."""
+    if t.dtype not in _DTYPE_CODE:
+        raise TypeError(f"oracle takes fp16/bf16 tensors, got {t.dtype}")
+    return np.ascontiguousarray(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+class Oracle:
+    """One loaded copy of the oracle library (a path lets tests load variants)."""
+
+    def __init__(self, path=DEFAULT_LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"{path} is not built; run oracle/build.py")
+        lib = ctypes.CDLL(path)
+        lib.oracle_attention_rows.restype = ctypes.c_int
+        lib.oracle_attention_rows.argtypes = [
+            _u16p, _u16p, _u16p, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64,
+            _f64p, _f64p, ctypes.c_int]
+        lib.oracle_combine.restype = ctypes.c_int
+        lib.oracle_combine.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                       _f64p, _f64p]
+        lib.oracle_decode_f16.restype = ctypes.c_double
+        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_bf16.restype = ctypes.c_double
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        self.lib = lib
+        self.path = path
+
+    # -- decoders ---------------------------------------------------------
+    def decode(self, bits, dtype):
+        f = self.lib.oracle_decode_bf16 if dtype == torch.bfloat16 else self.lib.oracle_decode_f16
+        return np.array([f(int(b)) for b in np.asarray(bits, dtype=np.uint16).ravel()])
+
+    # -- attention --------------------------------------------------------
+    def attention(self, q, k, v, causal, scale, rows=None, key_range=None, nthreads=None):
+        """fp64 attention of [B,H,Nq,d] queries against [B,H,Nk,d] keys/values.
+
+        rows: optional flat row indices (b*H + h)*Nq + i; then o is [len(rows), d]
+        and lse is [len(rows)], otherwise o is [B,H,Nq,d] and lse [B,H,Nq].
+        key_range: optional (begin, end) restricting the keys (split-KV partials).
+        """
+        if q.dtype != k.dtype or q.dtype != v.dtype:
+            raise TypeError("q, k, v must share a dtype")
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
+        if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+            raise ValueError("k and v must be [B, H, Nk, d] matching q")
+        qb, kb, vb = _bits(q), _bits(k), _bits(v)
+        kr = (0, Nk) if key_range is None else key_range
+        if rows is None:
+            nrows = B * H * Nq
+            rows_arr = None
+            o = np.empty((nrows, d), dtype=np.float64)
+        else:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            nrows = rows_arr.size
+            o = np.empty((nrows, d), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rc = self.lib.oracle_attention_rows(
+            _ptr(qb, _u16p), _ptr(kb, _u16p), _ptr(vb, _u16p), _DTYPE_CODE[q.dtype],
+            B, H, Nq, Nk, d, int(bool(causal)), float(scale), int(kr[0]), int(kr[1]),
+            _ptr(rows_arr, _i64p) if rows_arr is not None else None, nrows,
+            _ptr(o, _f64p), _ptr(lse, _f64p), nthreads or default_threads())
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_rows failed ({rc})")
+        if rows is None:
+            return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+        return o, lse
+
+    # -- split-KV ---------------------------------------------------------
+    @staticmethod
+    def split_ranges(Nk, num_splits):
+        """Contiguous key chunks of ceil(Nk / S) keys; trailing splits may be empty."""
+        chunk = -(-Nk // num_splits)
+        return [(min(Nk, s * chunk), min(Nk, (s + 1) * chunk)) for s in range(num_splits)]
+
+    def split_partials(self, q, k, v, causal, scale, num_splits, rows=None, nthreads=None):
+        """Per-split normalised (O_s, LSE_s): attention restricted to each key chunk."""
+        outs, lses = [], []
+        for kr in self.split_ranges(k.shape[2], num_splits):
+            o, l = self.attention(q, k, v, causal, scale, rows=rows, key_range=kr, nthreads=nthreads)
+            outs.append(o)
+            lses.append(l)
+        return np.stack(outs), np.stack(lses)
+
+    def combine(self, o_part, lse_part):
+        """LSE-weighted merge of [S, ..., d] partials into [..., d] and [...]."""
+        o_part = np.ascontiguousarray(np.asarray(o_part, dtype=np.float64))
+        lse_part = np.ascontiguousarray(np.asarray(lse_part, dtype=np.float64))
+        S, d = o_part.shape[0], o_part.shape[-1]
+        rest = lse_part.shape[1:]
+        R = int(np.prod(rest)) if rest else 1
+        if o_part.shape[:-1] != lse_part.shape:
+            raise ValueError("o_part must be lse_part's shape plus a trailing d")
+        o = np.empty((R, d), dtype=np.float64)
+        lse = np.empty((R,), dtype=np.float64)
+        rc = self.lib.oracle_combine(_ptr(o_part, _f64p), _ptr(lse_part, _f64p), S, R, d,
+                                     _ptr(o, _f64p), _ptr(lse, _f64p))
+        if rc != 0:
+            raise RuntimeError(f"oracle_combine failed ({rc})")
+        return o.reshape(*rest, d), lse.reshape(rest)
+
+
+_default = None
+
+
+def get():
+    """The oracle built from oracle/attention.c (loaded once)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+__all__ = ["Oracle", "get", "default_threads"]

@@ -1,0 +1,308 @@
+"""Pins that tie the fp64 oracle to facts outside itself.
+
+Each pin takes an `Oracle` and raises AssertionError when the oracle disagrees
+with what the pages and the mathematics fix.  The same pins run against the real
+oracle (must pass) and against deliberately broken copies (at least one must
+fail), so a plausible mistake anywhere in the oracle is caught.
+
+Sources for the facts used here:
+  Ringi, "Lecture 25", section 2.1 (safe softmax), section 2.2 (merge identity),
+  section 1.1 (three-step attention);  AIInfraGuide 6.2 "FlashAttention V2
+  explained", section 5.1 (causal mask, -inf before softmax) and its forward
+  pseudocode (L = m + log l);  LLM Infra Atlas "FA2: parallelism", section 4
+  (causal bound offset by seqlen_k - seqlen_q);  KingOfEgg "Flash Attention (4)",
+  section 3.5 (empty row: inv_sum = 1 so O = 0).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTYPES = (torch.float16, torch.bfloat16)
+
+
+def _close(a, b, atol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    inf_a, inf_b = np.isinf(a), np.isinf(b)
+    assert np.array_equal(inf_a, inf_b) and np.array_equal(a[inf_a], b[inf_b]), f"{what}: infinities differ"
+    assert not np.isnan(a).any() and not np.isnan(b).any(), f"{what}: NaN"
+    fin = ~inf_a
+    err = np.max(np.abs(a[fin] - b[fin]), initial=0.0)
+    assert err <= atol, f"{what}: max abs err {err:.3e} > {atol:.1e}"
+
+
+def _rand(shape, dtype, seed, lo=None, hi=None, step=None):
+    g = torch.Generator().manual_seed(seed)
+    if step is None:
+        return torch.randn(shape, generator=g).to(dtype)
+    n = torch.randint(int(lo / step), int(hi / step) + 1, shape, generator=g)
+    return (n.double() * step).to(dtype)     # exactly representable grid values
+
+
+def _visible(Nq, Nk, causal):
+    """[Nq, Nk] boolean visibility: key j < Nk, and j <= i + Nk - Nq when causal."""
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    vis = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        vis &= j <= i + (Nk - Nq)
+    return vis
+
+
+def library_reference(q, k, v, causal, scale):
+    """Attention from numpy matmul + scipy's logsumexp/softmax (fp64)."""
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    sigma = float(np.float32(scale))
+    s = sigma * (qd @ np.swapaxes(kd, -1, -2))
+    vis = _visible(q.shape[2], k.shape[2], causal)
+    s = np.where(vis, s, -np.inf)
+    empty = ~vis.any(axis=1)                                   # [Nq]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        lse = scipy.special.logsumexp(s, axis=-1)
+        p = scipy.special.softmax(np.where(empty[:, None], 0.0, s), axis=-1)
+    o = p @ vd
+    o[..., empty, :] = 0.0
+    lse[..., empty] = -np.inf
+    return o, lse
+
+
+CASES = [  # B, H, Nq, Nk, d, causal
+    (1, 2, 7, 13, 8, False), (1, 2, 7, 13, 8, True), (2, 1, 16, 16, 4, True),
+    (1, 1, 1, 5, 16, False), (1, 2, 33, 16, 8, True), (1, 1, 3, 40, 8, True),
+    (2, 2, 20, 20, 64, False), (1, 1, 9, 9, 128, True),
+]
+SCALES = (None, 0.37, -0.5, 2.0)
+
+
+def pin_library_reference(orc):
+    """Every case and scale matches numpy/scipy attention to 1e-12."""
+    n = 0
+    for ci, (B, H, Nq, Nk, d, causal) in enumerate(CASES):
+        for dt in DTYPES:
+            for sc in SCALES:
+                scale = 1 / math.sqrt(d) if sc is None else sc
+                q = _rand((B, H, Nq, d), dt, 100 + n)
+                k = _rand((B, H, Nk, d), dt, 200 + n)
+                v = _rand((B, H, Nk, d), dt, 300 + n)
+                n += 1
+                o, lse = orc.attention(q, k, v, causal, scale, nthreads=2)
+                ro, rl = library_reference(q, k, v, causal, scale)
+                _close(o, ro, 1e-12, f"O case {ci} {dt} scale {scale}")
+                _close(lse, rl, 1e-11, f"LSE case {ci} {dt} scale {scale}")
+
+
+def pin_torch_sdpa(orc):
+    """O matches torch's fp64 scaled_dot_product_attention with an explicit mask."""
+    for ci, (B, H, Nq, Nk, d, causal) in enumerate(CASES):
+        vis = _visible(Nq, Nk, causal)
+        rows = vis.any(axis=1)
+        if not rows.any():
+            continue
+        q = _rand((B, H, Nq, d), torch.float16, 400 + ci)
+        k = _rand((B, H, Nk, d), torch.float16, 500 + ci)
+        v = _rand((B, H, Nk, d), torch.float16, 600 + ci)
+        scale = float(np.float32(1 / math.sqrt(d)))
+        o, _ = orc.attention(q, k, v, causal, scale, nthreads=2)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.double(), k.double(), v.double(), attn_mask=torch.from_numpy(vis), scale=scale)
+        _close(o[:, :, rows], ref.numpy()[:, :, rows], 1e-12, f"SDPA case {ci}")
+
+
+def pin_identical_keys(orc):
+    """All keys equal: O_i is the mean of the visible values, LSE_i = s_i + ln|V_i|."""
+    for causal in (False, True):
+        for dt in DTYPES:
+            B, H, Nq, Nk, d = 1, 2, 12, 17, 8
+            q = _rand((B, H, Nq, d), dt, 11)
+            k = _rand((B, H, 1, d), dt, 12).expand(B, H, Nk, d).contiguous()
+            v = _rand((B, H, Nk, d), dt, 13)
+            scale = 0.5
+            o, lse = orc.attention(q, k, v, causal, scale, nthreads=1)
+            vis = _visible(Nq, Nk, causal)
+            vd = v.double().numpy()
+            cnt = vis.sum(axis=1)
+            exp_o = np.einsum("ij,bhjd->bhid", vis.astype(np.float64), vd) / np.maximum(cnt, 1)[:, None]
+            s = scale * np.einsum("bhid,bhd->bhi", q.double().numpy(), k.double().numpy()[:, :, 0])
+            with np.errstate(divide="ignore"):
+                exp_l = np.where(cnt > 0, s + np.log(cnt), -np.inf)
+            exp_o[:, :, cnt == 0] = 0.0
+            _close(o, exp_o, 1e-12, f"identical keys O causal={causal}")
+            _close(lse, exp_l, 1e-12, f"identical keys LSE causal={causal}")
+
+
+def pin_first_causal_row(orc):
+    """Nq == Nk causal: row 0 sees only key 0, so O_0 = v_0 and LSE_0 = sigma q_0.k_0;
+    the last row sees every key, so it equals the non-causal last row."""
+    for dt in DTYPES:
+        B, H, N, d = 2, 2, 24, 16
+        q, k, v = (_rand((B, H, N, d), dt, s) for s in (21, 22, 23))
+        o, lse = orc.attention(q, k, v, True, 0.25, nthreads=1)
+        on, ln = orc.attention(q, k, v, False, 0.25, nthreads=1)
+        _close(o[:, :, 0], v.double().numpy()[:, :, 0], 0.0, "first causal row O")
+        s0 = 0.25 * (q.double().numpy()[:, :, 0] * k.double().numpy()[:, :, 0]).sum(-1)
+        _close(lse[:, :, 0], s0, 1e-13, "first causal row LSE")
+        _close(o[:, :, -1], on[:, :, -1], 1e-13, "last causal row O")
+        _close(lse[:, :, -1], ln[:, :, -1], 1e-13, "last causal row LSE")
+
+
+def pin_scale_zero(orc):
+    """scale = 0: uniform weights, O_i = mean of visible v, LSE_i = ln |V_i|."""
+    for causal in (False, True):
+        B, H, Nq, Nk, d = 1, 1, 10, 6, 8
+        q, k, v = (_rand((B, H, n, d), torch.bfloat16, s) for n, s in ((Nq, 31), (Nk, 32), (Nk, 33)))
+        o, lse = orc.attention(q, k, v, causal, 0.0, nthreads=1)
+        vis = _visible(Nq, Nk, causal)
+        cnt = vis.sum(axis=1)
+        exp_o = (vis.astype(np.float64) @ v.double().numpy()[0, 0]) / np.maximum(cnt, 1)[:, None]
+        with np.errstate(divide="ignore"):
+            exp_l = np.where(cnt > 0, np.log(np.maximum(cnt, 1)), -np.inf)
+        _close(o[0, 0], exp_o, 1e-13, f"scale 0 O causal={causal}")
+        _close(lse[0, 0], exp_l, 1e-13, f"scale 0 LSE causal={causal}")
+
+
+def pin_key_shift(orc):
+    """Adding u to every key shifts s_ij by sigma q_i.u for all j: O is unchanged and
+    LSE_i moves by sigma q_i.u (softmax(S + c_i) = softmax(S))."""
+    for causal in (False, True):
+        for dt in DTYPES:
+            B, H, Nq, Nk, d = 1, 2, 9, 14, 8
+            q = _rand((B, H, Nq, d), dt, 41, -2, 2, 0.125)
+            k = _rand((B, H, Nk, d), dt, 42, -3, 3, 0.125)
+            u = _rand((1, 1, 1, d), dt, 43, -1, 1, 0.125)
+            v = _rand((B, H, Nk, d), dt, 44)
+            k2 = (k.double() + u.double()).to(dt)
+            assert torch.equal(k2.double(), k.double() + u.double()), "shift not exact"
+            o1, l1 = orc.attention(q, k, v, causal, 0.3, nthreads=1)
+            o2, l2 = orc.attention(q, k2, v, causal, 0.3, nthreads=1)
+            shift = float(np.float32(0.3)) * (q.double().numpy() @ u.double().numpy()[0, 0, 0])
+            _close(o2, o1, 1e-12, "key shift O")
+            _close(l2, l1 + shift, 1e-12, "key shift LSE")
+
+
+def pin_value_shift(orc):
+    """Adding w to every value row adds w to every non-empty output row."""
+    for causal in (False, True):
+        B, H, Nq, Nk, d = 1, 1, 8, 11, 16
+        q = _rand((B, H, Nq, d), torch.float16, 51)
+        k = _rand((B, H, Nk, d), torch.float16, 52)
+        v = _rand((B, H, Nk, d), torch.float16, 53, -2, 2, 0.125)
+        w = _rand((1, 1, 1, d), torch.float16, 54, -1, 1, 0.125)
+        v2 = (v.double() + w.double()).to(torch.float16)
+        o1, _ = orc.attention(q, k, v, causal, 0.7, nthreads=1)
+        o2, _ = orc.attention(q, k, v2, causal, 0.7, nthreads=1)
+        _close(o2, o1 + w.double().numpy()[0, 0], 1e-12, "value shift")
+
+
+def pin_key_permutation(orc):
+    """Non-causal attention is invariant to a joint permutation of keys and values."""
+    B, H, Nq, Nk, d = 2, 1, 5, 19, 8
+    q, k, v = (_rand((B, H, n, d), torch.float16, s) for n, s in ((Nq, 61), (Nk, 62), (Nk, 63)))
+    perm = torch.randperm(Nk, generator=torch.Generator().manual_seed(64))
+    o1, l1 = orc.attention(q, k, v, False, 0.4, nthreads=1)
+    o2, l2 = orc.attention(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False, 0.4, nthreads=1)
+    _close(o2, o1, 1e-13, "permutation O")
+    _close(l2, l1, 1e-13, "permutation LSE")
+
+
+def pin_empty_rows(orc):
+    """Causal with Nq > Nk: rows i < Nq - Nk see no key (O = 0, LSE = -inf)."""
+    B, H, Nq, Nk, d = 1, 1, 20, 8, 8
+    q, k, v = (_rand((B, H, n, d), torch.float16, s) for n, s in ((Nq, 71), (Nk, 72), (Nk, 73)))
+    o, lse = orc.attention(q, k, v, True, 0.5, nthreads=1)
+    assert np.all(o[0, 0, :12] == 0.0) and np.all(lse[0, 0, :12] == -np.inf), "empty rows"
+    assert np.all(np.isfinite(lse[0, 0, 12:])), "non-empty rows must be finite"
+    # row 12 sees exactly key 0
+    _close(o[0, 0, 12], v.double().numpy()[0, 0, 0], 0.0, "first non-empty row")
+
+
+def pin_dominant_score(orc):
+    """When one score leads the rest by > 100 nats, O_i = v_argmax and LSE_i = max s
+    (to double rounding) -- also forces scores far beyond exp's range."""
+    B, H, Nq, Nk, d = 1, 1, 3, 9, 4
+    q = torch.zeros((B, H, Nq, d))
+    q[0, 0, :, 0] = torch.tensor([1.0, -1.0, 2.0])
+    k = torch.zeros((B, H, Nk, d))
+    k[0, 0, :, 0] = torch.arange(Nk) / 4.0
+    v = _rand((B, H, Nk, d), torch.float16, 81)
+    q, k = q.half(), k.half()
+    o, lse = orc.attention(q, k, v, False, 512.0, nthreads=1)
+    vd = v.double().numpy()[0, 0]
+    exp_o = np.stack([vd[Nk - 1], vd[0], vd[Nk - 1]])
+    exp_l = np.array([512.0 * (Nk - 1) / 4.0, 0.0, 512.0 * 2 * (Nk - 1) / 4.0])
+    _close(o[0, 0], exp_o, 1e-15, "dominant score O")
+    _close(lse[0, 0], exp_l, 1e-12, "dominant score LSE")
+
+
+def pin_decoders(orc):
+    """All 65536 patterns of each format decode as numpy/torch convert them."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt in DTYPES:
+        mine = orc.decode(bits, dt)
+        ref = torch.from_numpy(bits.view(np.int16)).view(dt).double().numpy()
+        nan_m, nan_r = np.isnan(mine), np.isnan(ref)
+        assert np.array_equal(nan_m, nan_r), f"{dt}: NaN patterns differ"
+        assert np.array_equal(mine[~nan_m], ref[~nan_r]), f"{dt}: decoded values differ"
+
+
+def pin_split_combine(orc):
+    """Merging per-split partials reproduces unsplit attention (merge identity)."""
+    for causal in (False, True):
+        B, H, Nq, Nk, d = 1, 2, 6, 37, 8
+        q, k, v = (_rand((B, H, n, d), torch.float16, s) for n, s in ((Nq, 91), (Nk, 92), (Nk, 93)))
+        o, lse = orc.attention(q, k, v, causal, 0.6, nthreads=1)
+        for S in (1, 2, 16, 17, 37):
+            op, lp = orc.split_partials(q, k, v, causal, 0.6, S, nthreads=1)
+            oc, lc = orc.combine(op, lp)
+            _close(oc, o, 1e-12, f"combine O S={S} causal={causal}")
+            _close(lc, lse, 1e-12, f"combine LSE S={S} causal={causal}")
+
+
+def pin_combine_closed_form(orc):
+    """Two splits with l ratio 1:3 (LSE 0 and ln 3): O = (O_1 + 3 O_2)/4, LSE = ln 4;
+    an all-empty row gives O = 0, LSE = -inf; one split is the identity."""
+    op = np.array([[[1.0, 0.0], [5.0, 6.0]], [[0.0, 1.0], [7.0, 8.0]]])   # [S=2, R=2, d=2]
+    lp = np.array([[0.0, -np.inf], [math.log(3.0), -np.inf]])
+    o, lse = orc.combine(op, lp)
+    _close(o, np.array([[0.25, 0.75], [0.0, 0.0]]), 1e-15, "combine closed form O")
+    _close(lse, np.array([math.log(4.0), -np.inf]), 1e-15, "combine closed form LSE")
+    o1, l1 = orc.combine(op[:1, :1], lp[:1, :1])
+    _close(o1, op[0, :1], 0.0, "combine identity O")
+    _close(l1, lp[0, :1], 0.0, "combine identity LSE")
+
+
+def _eval(expr):
+    if isinstance(expr, (int, float)):
+        return float(expr)
+    return float(eval(expr, {"__builtins__": {}}, {"exp": math.exp, "log": math.log, "inf": math.inf}))
+
+
+def pin_worked_examples(orc):
+    """Hand-derived examples in tests/golden/worked_examples.json."""
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        doc = json.load(f)
+    for ex in doc["examples"]:
+        dt = {"f16": torch.float16, "bf16": torch.bfloat16}[ex["dtype"]]
+        if ex["kind"] == "attention":
+            q, k, v = (torch.tensor(ex[n], dtype=torch.float64)[None, None].to(dt) for n in ("q", "k", "v"))
+            o, lse = orc.attention(q, k, v, ex["causal"], ex["scale"], nthreads=1)
+            exp_o = np.array([[_eval(x) for x in row] for row in ex["O"]])
+            exp_l = np.array([_eval(x) for x in ex["LSE"]])
+            _close(o[0, 0], exp_o, 1e-14, ex["name"])
+            _close(lse[0, 0], exp_l, 1e-14, ex["name"])
+        else:
+            o, lse = orc.combine(np.array(ex["o_part"], dtype=np.float64),
+                                 np.array([[_eval(x) for x in s] for s in ex["lse_part"]]))
+            _close(o, np.array([[_eval(x) for x in r] for r in ex["O"]]), 1e-14, ex["name"])
+            _close(lse, np.array([_eval(x) for x in ex["LSE"]]), 1e-14, ex["name"])
+
+
+ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
+            pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
+            pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
+            pin_worked_examples]

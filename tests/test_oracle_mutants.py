@@ -1,0 +1,53 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+at least one pin catches each: evidence that the pins constrain every part of
+the oracle -- the scores, the mask, the softmax, the LSE, the decoders and the
+split merge."""
+import os
+
+import pytest
+
+from oracle import build, oracle
+from tests import oracle_pins
+
+MUTANTS = [
+    ("drop_scale", "s[j - lo] = jb->sigma * acc;", "s[j - lo] = acc;"),
+    ("score_sign", "acc += qrow[t] * decode", "acc -= qrow[t] * decode"),
+    ("causal_off_by_one", "(int64_t)i + (Nk - Nq) + 1;", "(int64_t)i + (Nk - Nq);"),
+    ("causal_offset_sign", "(int64_t)i + (Nk - Nq) + 1;", "(int64_t)i - (Nk - Nq) + 1;"),
+    ("causal_top_left", "(int64_t)i + (Nk - Nq) + 1;", "(int64_t)i + 1;"),
+    ("no_max_subtraction", "double p = exp(s[j - lo] - m);", "double p = exp(s[j - lo]);"),
+    ("lse_without_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("lse_without_log", "*lse_out = m + log(l);", "*lse_out = m + l;"),
+    ("unnormalised_output", "for (int t = 0; t < d; ++t) o_row[t] /= l;", "for (int t = 0; t < d; ++t) o_row[t] /= 1.0;"),
+    ("k_row_stride", "const uint16_t *kj = kp + (size_t)j * d;", "const uint16_t *kj = kp + (size_t)j;"),
+    ("v_row_of_query", "const uint16_t *vj = vp + (size_t)j * d;", "const uint16_t *vj = vp + (size_t)i * d;"),
+    ("q_row_of_key", "jb->q + ((size_t)bh * Nq + i) * d;", "jb->q + ((size_t)bh * Nq) * d;"),
+    ("head_stride", "const uint16_t *kp = jb->k + (size_t)bh * Nk * d;", "const uint16_t *kp = jb->k;"),
+    ("f16_exponent_bias", "expo - 25", "expo - 24"),
+    ("f16_subnormal", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    ("bf16_exponent_bias", "expo - 134", "expo - 133"),
+    ("key_range_ignored", "int lo = jb->key_begin < 0 ? 0 : jb->key_begin;", "int lo = 0;"),
+    ("combine_weight_sign", "double w = exp(ls - M);", "double w = exp(M - ls);"),
+    ("combine_lse_missing_max", "lse[r] = M + log(wsum);", "lse[r] = log(wsum);"),
+    ("combine_skip_normalise", "for (int t = 0; t < d; ++t) orow[t] /= wsum;", "for (int t = 0; t < d; ++t) orow[t] /= 1.0;"),
+    ("empty_row_lse_zero", "if (hi <= lo) { *lse_out = -INFINITY; return; }", "if (hi <= lo) { *lse_out = 0.0; return; }"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    with open(build.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"pattern for {name} must occur exactly once"
+    mpath = os.path.join(tmp_path, f"{name}.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = build.build(src=mpath, out=os.path.join(tmp_path, f"lib{name}.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, RuntimeError, FloatingPointError) as e:
+            caught.append(f"{pin.__name__}: {str(e)[:80]}")
+    assert caught, f"no pin catches the mutant {name}"
