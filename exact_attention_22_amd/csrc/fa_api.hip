@@ -1,0 +1,109 @@
+// fa_api.hip -- the C ABI of libfa.so (declared in include/fa.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// then enqueues its kernels on the caller's stream and returns.  The library
+// allocates, frees and synchronises nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+// Element count a*b*c*d, or -1 when it leaves int64 or is non-positive.
+int64_t count4(int64_t a, int64_t b, int64_t c, int64_t d) {
+    if (a <= 0 || b <= 0 || c <= 0 || d <= 0) return -1;
+    const int64_t lim = INT64_MAX / 8;
+    int64_t x = a;
+    for (int64_t f : {b, c, d}) {
+        if (x > lim / f) return -1;
+        x *= f;
+    }
+    return x;
+}
+
+fa_status check_common(int B, int H, int Nq, int Nk, int d, float scale, fa_dtype dtype) {
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+    if (count4(B, H, Nq, d) < 0 || count4(B, H, Nk, d) < 0) return FA_ERR_SHAPE;
+    if ((int64_t)B * H > INT32_MAX) return FA_ERR_SHAPE;
+    if (!isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                 fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, dtype == FA_BF16, scale, 0};
+    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+}
+
+size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
+    if (!supported_d(d) || num_splits < 1) return 0;
+    const int64_t n = count4(num_splits, B, H, Nq);
+    if (n < 0 || n > INT64_MAX / 4 / (d + 1)) return 0;
+    return (size_t)n * (size_t)(d + 1) * 4u;
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                         int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                         int num_splits, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
+    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (num_splits < 1 || num_splits > Nk) return FA_ERR_SHAPE;
+    if (count4(num_splits, B, H, (int64_t)Nq * d) < 0) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) || ((uintptr_t)lse_part & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k, v, o_part, lse_part, B, H, Nq, Nk, d, causal != 0, dtype == FA_BF16, scale,
+                    num_splits};
+    // One query row sees every key whatever the causal flag (j <= 0 + Nk - 1):
+    // the streaming kernel serves it; longer query blocks use the tiled kernel.
+    if (Nq == 1) return from_hip(fa::launch_decode(p, (hipStream_t)stream));
+    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+}
+
+fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                             int B, int H, int Nq, int d, int num_splits, fa_dtype dtype, void* stream) {
+    if (!o_part || !lse_part || !o || !lse) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Nq < 1 || num_splits < 1) return FA_ERR_SHAPE;
+    const int64_t rows = count4(B, H, Nq, 1);
+    if (rows < 0 || count4(num_splits, rows, d, 1) < 0) return FA_ERR_SHAPE;
+    if (((uintptr_t)o_part & 3u) || ((uintptr_t)lse_part & 3u) || ((uintptr_t)o & 1u) || ((uintptr_t)lse & 3u))
+        return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_combine(o_part, lse_part, o, lse, rows, d, num_splits, dtype == FA_BF16,
+                                       (hipStream_t)stream));
+}
+
+const char* fa_status_str(fa_status status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid size: B, H, Nq, Nk must be >= 1, 1 <= num_splits <= Nk, no overflow";
+        case FA_ERR_UNSUPPORTED: return "unsupported: d must be 64 or 128, dtype f16/bf16, finite scale, 16-byte aligned tensors";
+        case FA_ERR_WORKSPACE: return "workspace too small";
+        case FA_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

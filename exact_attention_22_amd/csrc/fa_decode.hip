@@ -1,0 +1,237 @@
+// fa_decode.hip -- split-KV partials for a single query row per head (decode).
+//
+// With seqlen_q = 1 a grid over query tiles has only B*H workgroups, so the keys
+// are split into num_splits chunks that run in parallel, each producing a
+// normalised partial (O, LSE) that a combine kernel merges (LLM Infra Atlas
+// "FA2: parallelism", section 2; Ringi "Lecture 25", section 0.3).
+//
+// gfx950 design (not from the pages): the work is ~1 FLOP per byte, so this is
+// a streaming kernel, not a matrix one.  One workgroup (4 wavefronts) owns one
+// (b, h, split).  A key row of D 16-bit values is spread over D/8 lanes, 16
+// bytes each, so every load instruction of a wavefront reads 1 KiB of
+// consecutive memory (4 rows at d = 128, 8 at d = 64).  The dot product is
+// finished with DPP row operations, every lane of the row keeps the online
+// softmax state of its row, and each lane accumulates its own 8 output values.
+// Eight groups of keys are loaded per step so that enough bytes are in flight
+// to cover HBM latency.  At the end the 16 (d = 128) or 32 (d = 64) partial
+// states of the workgroup merge through LDS with the online-softmax identity
+// (Ringi, Lecture 25, section 2.2).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+struct DecArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    float* o_part;
+    float* lse_part;
+    int BH, Nk, S;
+    int split_chunk;
+    float c;   // scale * log2(e), sign included
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the CH lanes that hold one key row (CH = 16 or 8, aligned groups).
+template <int CH>
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp_mov<0xB1>(x);          // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);          // quad_perm [2,3,0,1]
+    if constexpr (CH == 16) {
+        x += dpp_mov<0x124>(x);     // row_ror:4
+        x += dpp_mov<0x128>(x);     // row_ror:8
+    } else {
+        x += dpp_mov<0x141>(x);     // row_half_mirror
+    }
+    return x;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen8(u32x4 x, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = widen<BF16>((uint16_t)(x[i] & 0xffff));
+        f[2 * i + 1] = widen<BF16>((uint16_t)(x[i] >> 16));
+    }
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
+    constexpr int CH = D / 8;          // lanes per key row
+    constexpr int KPI = 64 / CH;       // key rows per wavefront load
+    constexpr int U = 8;               // key groups in flight per step
+    constexpr int NP = 4 * KPI;        // partial states per workgroup
+    __shared__ float s_m[NP], s_l[NP];
+    __shared__ __attribute__((aligned(16))) float s_o[NP * D];
+
+    const int split = blockIdx.x % a.S;
+    const int bh = blockIdx.x / a.S;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c = lane % CH, r = lane / CH;
+
+    const int ks = min(a.Nk, split * a.split_chunk);
+    const int ke = min(a.Nk, ks + a.split_chunk);
+    const int ngroups = (ke - ks + KPI - 1) / KPI;
+
+    const uint16_t* kg = a.k + (size_t)bh * a.Nk * D;
+    const uint16_t* vg = a.v + (size_t)bh * a.Nk * D;
+
+    float qv[8];
+    widen8<BF16>(*(const u32x4*)(a.q + (size_t)bh * D + 8 * c), qv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] *= a.c;
+
+    float M = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+
+    for (int g0 = w; g0 < ngroups; g0 += 4 * U) {
+        u32x4 kr[U], vr[U];
+        int key[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            key[u] = ks + (g0 + 4 * u) * KPI + r;
+            if (key[u] < ke) {
+                kr[u] = *(const u32x4*)(kg + (size_t)key[u] * D + 8 * c);
+                vr[u] = *(const u32x4*)(vg + (size_t)key[u] * D + 8 * c);
+            } else {
+                kr[u] = u32x4{0, 0, 0, 0};
+                vr[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+        float s[U];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[8];
+            widen8<BF16>(kr[u], kf);
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qv[i], kf[i], part);
+            s[u] = row_sum<CH>(part);
+            if (key[u] >= ke) s[u] = -INFINITY;
+            mx = fmaxf(mx, s[u]);
+        }
+        const float Mn = fmaxf(M, mx);
+        const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M - Mn);
+        M = Mn;
+        const float Mg = (M == -INFINITY) ? 0.f : M;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = exp2_fast(s[u] - Mg);
+            l += p;
+            float vf[8];
+            widen8<BF16>(vr[u], vf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(p, vf[i], acc[i]);
+        }
+    }
+
+    // merge the workgroup's partial states
+    const int pidx = w * KPI + r;
+    if (c == 0) {
+        s_m[pidx] = M;
+        s_l[pidx] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_o[pidx * D + 8 * c + i] = acc[i];
+    __syncthreads();
+    if (tid < D) {
+        float Ms = -INFINITY;
+        for (int i = 0; i < NP; ++i) Ms = fmaxf(Ms, s_m[i]);
+        float den = 0.f, num = 0.f;
+        for (int i = 0; i < NP; ++i) {
+            const float wgt = (s_m[i] == -INFINITY) ? 0.f : exp2_fast(s_m[i] - Ms);
+            den = __builtin_fmaf(wgt, s_l[i], den);
+            num = __builtin_fmaf(wgt, s_o[i * D + tid], num);
+        }
+        const size_t row = (size_t)split * a.BH + bh;
+        a.o_part[row * D + tid] = den > 0.f ? num / den : 0.f;
+        if (tid == 0) a.lse_part[row] = den > 0.f ? (Ms + log2f(den)) * kLn2 : -INFINITY;
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ op, const float* __restrict__ lp,
+                                                      uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                      int64_t R, int S, int D) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= R) return;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(size_t)s * R + row]);
+    const int nd = D / 64;   // values per lane (1 or 2)
+    float num[2] = {0.f, 0.f};
+    float den = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < S; ++s) {
+            const float ls = lp[(size_t)s * R + row];
+            if (ls == -INFINITY) continue;
+            const float wgt = exp2_fast((ls - M) * kLog2e);
+            den += wgt;
+            const float* src = op + ((size_t)s * R + row) * D;
+            for (int j = 0; j < nd; ++j) num[j] = __builtin_fmaf(wgt, src[lane + 64 * j], num[j]);
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int j = 0; j < nd; ++j) {
+        const float x = num[j] * inv;
+        uint16_t bits;
+        if constexpr (BF16)
+            bits = __builtin_bit_cast(uint16_t, (__bf16)x);
+        else
+            bits = __builtin_bit_cast(uint16_t, (_Float16)x);
+        o[row * D + lane + 64 * j] = bits;
+    }
+    if (lane == 0) lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
+    DecArgs a;
+    a.q = (const uint16_t*)p.q;
+    a.k = (const uint16_t*)p.k;
+    a.v = (const uint16_t*)p.v;
+    a.o_part = (float*)p.o;
+    a.lse_part = p.lse;
+    a.BH = p.B * p.H;
+    a.Nk = p.Nk;
+    a.S = p.num_splits;
+    a.split_chunk = split_chunk(p.Nk, p.num_splits);
+    a.c = p.scale * kLog2e;
+    const int64_t blocks = (int64_t)a.BH * a.S;
+    if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (p.d == 128) {
+        if (p.bf16) hipLaunchKernelGGL((decode_kernel<true, 128>), dim3((int)blocks), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<false, 128>), dim3((int)blocks), dim3(256), 0, stream, a);
+    } else {
+        if (p.bf16) hipLaunchKernelGGL((decode_kernel<true, 64>), dim3((int)blocks), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<false, 64>), dim3((int)blocks), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                          int64_t rows, int d, int num_splits, bool bf16, hipStream_t stream) {
+    const int64_t blocks = (rows + 3) / 4;
+    if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL((combine_kernel<true>), dim3((int)blocks), dim3(256), 0, stream, o_part, lse_part,
+                           (uint16_t*)o, lse, rows, num_splits, d);
+    else
+        hipLaunchKernelGGL((combine_kernel<false>), dim3((int)blocks), dim3(256), 0, stream, o_part, lse_part,
+                           (uint16_t*)o, lse, rows, num_splits, d);
+    return hipGetLastError();
+}
+
+}  // namespace fa

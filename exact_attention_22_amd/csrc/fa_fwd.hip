@@ -1,0 +1,347 @@
+// fa_fwd.hip -- FlashAttention-2 forward on gfx950 MFMA (prefill and split-KV
+// partials for any Nq).
+//
+// Method (the pages this follows):
+//   * Q outer, KV inner: one workgroup owns one tile of Br = 128 query rows of
+//     one (b, h) and walks the key tiles; O stays on chip and is written once
+//     (AIInfraGuide 6.2 "FlashAttention V2 explained", section 2; LLM Infra
+//     Atlas "FA2: parallelism", section 2: grid over query tiles x batch x heads).
+//   * split-Q: each of the 4 wavefronts owns 32 query rows and computes their
+//     whole softmax, so waves never reduce across each other (LLM Infra Atlas,
+//     section 3; AIInfraGuide 6.2, section 4).
+//   * online softmax with an unnormalised accumulator: O <- alpha*O + P V and
+//     l <- alpha*l + rowsum(P), divided by l once at the end (Ringi, "Lecture 25",
+//     sections 2.2-2.3; AIInfraGuide 6.2, section 3.2).  exp is evaluated as
+//     exp2 with scale*log2(e) folded into one multiplier (LLM Infra Atlas,
+//     section 1; KingOfEgg "Flash Attention (4)", section 3.1).
+//   * causal: key tiles past the diagonal are never loaded; only tiles crossing
+//     the diagonal or the key tail are masked, and walking the tiles from the
+//     last one down puts those first (LLM Infra Atlas, section 4; KingOfEgg,
+//     section 3.2).
+//   * epilogue: inv = 1 when the row sum is 0 or NaN; LSE = max*scale + ln(sum)
+//     (KingOfEgg, section 3.5).
+//
+// gfx950 mapping (not from the pages):
+//   * S^T = K Q^T on v_mfma_f32_32x32x16: a lane's accumulator holds one query
+//     (lane % 32) against 16 of 32 keys, so the row max and row sum are in-lane
+//     plus one exchange between lane l and l^32 (v_permlane32_swap).
+//   * K rows enter the first product in an order with bits 2 and 3 of the key
+//     index swapped; then accumulator registers 8p..8p+7 of a lane are exactly
+//     the 8 consecutive keys 16p + 8*(lane/32) + 0..7 that lane must supply as
+//     the B operand of O^T = V^T P^T.  P goes from the first product's
+//     accumulator to the second product's operand with one v_cvt_pk per pair
+//     and no LDS round trip.
+//   * O^T accumulates in registers: each lane owns its query's output values,
+//     so the rescale by alpha is a per-lane multiply.
+//   * V stays row-major in LDS and ds_read_b64_tr_b16 produces the key-major
+//     operand.  K and V tiles are double-buffered in LDS through 16-byte
+//     coalesced global loads and an XOR swizzle (fa_device.h).
+//   * Lazy rescale: the exponent reference only moves (and O, l are only
+//     rescaled) when a row's new maximum exceeds it by more than 2^8 in
+//     probability, decided per wavefront.  Any reference gives the same
+//     O = sum 2^(t-M) v / sum 2^(t-M); keeping the reference at or below the
+//     true maximum keeps every P <= 256, well inside fp16 range.
+//   * Workgroups are ordered heaviest causal tile first and mapped so that
+//     consecutive tiles of one head share an XCD (and its L2).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int BR = 128;     // query rows per workgroup (4 waves x 32)
+constexpr int BC = 64;      // keys per tile
+constexpr float TAU = 8.0f; // lazy-rescale threshold, log2 units
+
+struct FwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    void* o;
+    float* lse;
+    int B, H, Nq, Nk;
+    int BH;
+    float c;           // |scale| * log2(e)
+    u32 qsign;         // 0x80008000 flips Q's sign when scale < 0
+    int n_qtiles;
+    int split_chunk;   // keys per split (split mode)
+};
+
+// Key index (within a 32-key block) that accumulator row i stands for: bits 2 and 3 swapped.
+__device__ __forceinline__ int perm_row(int i) {
+    return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+template <bool BF16, int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+    constexpr int ROWB = D * 2;                  // bytes per K/V row
+    constexpr int CHUNKS = D / 8;                // 16-byte chunks per row
+    constexpr int TILE = BC * ROWB;              // bytes per K (or V) tile
+    constexpr int NS = D / 16;                   // 16-wide d slices of Q
+    constexpr int ND = D / 32;                   // 32-wide d blocks of O^T
+    constexpr int LOADS = TILE / (256 * 16);     // 16-byte loads per thread per tensor per tile
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * TILE];
+
+    // ---- work item -------------------------------------------------------
+    const int total = gridDim.x;
+    int L = blockIdx.x;
+    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);   // XCD-contiguous ranges
+    const int qt = a.n_qtiles - 1 - (L % a.n_qtiles);             // heaviest first
+    const int rest = L / a.n_qtiles;
+    const int bh = rest % a.BH;
+    const int split = SPLIT ? rest / a.BH : 0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int q0 = qt * BR;
+    const int qw = q0 + 32 * w;
+    const int qi = qw + l32;
+    const int off = a.Nk - a.Nq;                  // causal: key j visible iff j <= i + off
+
+    const uint16_t* qg = a.q + (size_t)bh * a.Nq * D;
+    const uint16_t* kg = a.k + (size_t)bh * a.Nk * D;
+    const uint16_t* vg = a.v + (size_t)bh * a.Nk * D;
+
+    int ks = 0, ke = a.Nk;
+    if (SPLIT) {
+        ks = min(a.Nk, split * a.split_chunk);
+        ke = min(a.Nk, ks + a.split_chunk);
+    }
+    int hi = ke;
+    if (CAUSAL) hi = min(hi, min(a.Nq, q0 + BR) - 1 + off + 1);
+    const int n_tiles = hi > ks ? (hi - ks + BC - 1) / BC : 0;
+
+    // ---- Q fragments, resident for the whole key loop ----------------------
+    u32x4 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (qi < a.Nq) {
+            qf[s] = *(const u32x4*)(qg + (size_t)qi * D + 16 * s + 8 * h);
+            qf[s] ^= a.qsign;
+        } else {
+            qf[s] = u32x4{0, 0, 0, 0};
+        }
+    }
+
+    // ---- K/V staging: global -> registers -> LDS ----------------------------
+    u32x4 kr[LOADS], vr[LOADS];
+    auto gload = [&](int tile) {
+        const int k0 = ks + tile * BC;
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int idx = tid + 256 * u;
+            const int r = idx / CHUNKS, c = idx % CHUNKS;
+            const int key = k0 + r;
+            if (key < ke) {
+                kr[u] = *(const u32x4*)(kg + (size_t)key * D + 8 * c);
+                vr[u] = *(const u32x4*)(vg + (size_t)key * D + 8 * c);
+            } else {
+                kr[u] = u32x4{0, 0, 0, 0};
+                vr[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        unsigned char* kb = smem + buf * 2 * TILE;
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int idx = tid + 256 * u;
+            const int o = lds_off<D>(idx / CHUNKS, idx % CHUNKS);
+            *(u32x4*)(kb + o) = kr[u];
+            *(u32x4*)(kb + TILE + o) = vr[u];
+        }
+    };
+
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
+    float Mu = -INFINITY;   // exponent reference (log2 units of scaled scores)
+    float lsum = 0.f;       // this lane's half of the row sum, relative to Mu
+
+    const int krow0 = perm_row(l32);         // K row this lane feeds to S^T (within a 32-key block)
+    const int r4 = (lane & 15) >> 2;         // transpose-read row within a 4-row group
+    const int c4 = lane & 3;
+    const int g1 = (lane >> 4) & 1;
+
+    // One key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
+    // need_mask (wave-uniform) is set only for tiles that cross the chunk end
+    // or, for causal attention, the diagonal.
+    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, bool need_mask) {
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = f32x16{};
+            const int row = 32 * kb + krow0;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 kf = *(const u32x4*)(Kb + lds_off<D>(row, 2 * s + h));
+                sacc[kb] = mfma32<BF16>(kf, qf[s], sacc[kb]);
+            }
+        }
+        // register r of block kb holds key k0 + 8h + kofs(kb, r); it is visible
+        // iff kofs < bound (the chunk end and, for causal, the diagonal)
+        int bound = ke - k0 - 8 * h;
+        if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = -INFINITY;
+        }
+        // row max over this tile (raw scores), both lane halves
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        mx = max_halves(mx);
+        const float Mc = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+        if (__ballot(Mc > Mu + TAU)) {          // wave-uniform: move the reference
+            const float Mn = fmaxf(Mu, Mc);
+            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+            Mu = Mn;
+        }
+        const float Mg = (Mu == -INFINITY) ? 0.f : Mu;   // no -inf - -inf
+        // P = 2^(s*c - M)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
+        if (need_mask) {   // masked keys weigh exactly 0, also when scale is 0
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = 0.f;
+        }
+        // row sum in fp32, before P is rounded to 16 bits
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum += sacc[kb][r];
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const f32x16& P = sacc[kb];
+                const u32x4 pb = {pack2<BF16>(P[8 * p + 0], P[8 * p + 1]), pack2<BF16>(P[8 * p + 2], P[8 * p + 3]),
+                                  pack2<BF16>(P[8 * p + 4], P[8 * p + 5]), pack2<BF16>(P[8 * p + 6], P[8 * p + 7])};
+                const int row = 32 * kb + 16 * p + 8 * h + r4;
+#pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    const int chunk = 4 * db + 2 * g1 + (c4 >> 1);
+                    const int bo = (c4 & 1) * 8;
+                    const i16x4 lo = lds_read_tr16(Vb + lds_off<D>(row, chunk) + bo);
+                    const i16x4 hi4 = lds_read_tr16(Vb + lds_off<D>(row + 4, chunk) + bo);
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
+                    const u32x4 va = {l2[0], l2[1], h2[0], h2[1]};
+                    oacc[db] = mfma32<BF16>(va, pb, oacc[db]);
+                }
+            }
+    };
+
+    if (n_tiles > 0) {
+        gload(n_tiles - 1);
+        sstore(0);
+    }
+    __syncthreads();
+    const int qmax_w = min(qw + 31, a.Nq - 1);
+#pragma clang loop unroll(disable)
+    for (int it = 0; it < n_tiles; ++it) {
+        const int tile = n_tiles - 1 - it;
+        const int buf = it & 1;
+        if (it + 1 < n_tiles) gload(tile - 1);
+        const int k0 = ks + tile * BC;
+        const bool active = qw < a.Nq && (!CAUSAL || k0 <= qmax_w + off);
+        if (active) {
+            const unsigned char* Kb = smem + buf * 2 * TILE;
+            const bool need_mask = (k0 + BC > ke) || (CAUSAL && k0 + BC - 1 > qw + off);
+            tile_step(Kb, Kb + TILE, k0, need_mask);
+        }
+        if (it + 1 < n_tiles) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue -------------------------------------------------------------
+    const float lt = sum_halves(lsum);
+    const float inv = (lt == 0.f || lt != lt) ? 1.f : 1.f / lt;
+    const float lse_v = (lt == 0.f) ? -INFINITY : (Mu + log2f(lt)) * kLn2;
+    if (qi < a.Nq) {
+        if constexpr (SPLIT) {
+            float* op = (float*)a.o + (((size_t)split * a.BH + bh) * a.Nq + qi) * D;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v4 = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                      oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+                    *(f32x4*)(op + 32 * db + 8 * g + 4 * h) = v4;
+                }
+            if (h == 0) a.lse[((size_t)split * a.BH + bh) * a.Nq + qi] = lse_v;
+        } else {
+            uint16_t* op = (uint16_t*)a.o + ((size_t)bh * a.Nq + qi) * D;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2 v2 = {pack2<BF16>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                      pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
+                }
+            if (h == 0) a.lse[(size_t)bh * a.Nq + qi] = lse_v;
+        }
+    }
+}
+
+template <bool BF16, int D, bool CAUSAL, bool SPLIT>
+hipError_t launch_t(const FwdArgs& a, int blocks, hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, SPLIT>), dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, bool split, hipStream_t s) {
+    if (causal)
+        return split ? launch_t<BF16, D, true, true>(a, blocks, s) : launch_t<BF16, D, true, false>(a, blocks, s);
+    return split ? launch_t<BF16, D, false, true>(a, blocks, s) : launch_t<BF16, D, false, false>(a, blocks, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+    FwdArgs a;
+    a.q = (const uint16_t*)p.q;
+    a.k = (const uint16_t*)p.k;
+    a.v = (const uint16_t*)p.v;
+    a.o = p.o;
+    a.lse = p.lse;
+    a.B = p.B;
+    a.H = p.H;
+    a.Nq = p.Nq;
+    a.Nk = p.Nk;
+    a.BH = p.B * p.H;
+    a.c = fabsf(p.scale) * kLog2e;
+    a.qsign = p.scale < 0.f ? 0x80008000u : 0u;
+    a.n_qtiles = (p.Nq + BR - 1) / BR;
+    const bool split = p.num_splits > 0;
+    const int S = split ? p.num_splits : 1;
+    a.split_chunk = split_chunk(p.Nk, S);
+    const int64_t blocks = (int64_t)a.n_qtiles * a.BH * S;
+    if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (p.d == 128)
+        return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, split, stream)
+                      : dispatch_cs<false, 128>(a, (int)blocks, p.causal, split, stream);
+    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, split, stream)
+                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, split, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,32 @@
+// fa_launch.h -- host-side launchers behind the C ABI (internal to libfa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Validated arguments of one forward launch.  In split mode `o` is the fp32
+// o_part buffer and `lse` is lse_part; otherwise `o` holds dtype values.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, Nq, Nk, d;
+    bool causal;
+    bool bf16;
+    float scale;
+    int num_splits;   // 0: plain forward; >= 1: split-KV partials
+};
+
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_decode(const FwdParams& p, hipStream_t stream);
+hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                          int64_t rows, int d, int num_splits, bool bf16, hipStream_t stream);
+
+// Keys per split chunk: ceil(Nk / num_splits).
+inline int split_chunk(int Nk, int num_splits) { return (Nk + num_splits - 1) / num_splits; }
+
+}  // namespace fa

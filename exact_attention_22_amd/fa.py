@@ -1,0 +1,153 @@
+"""Thin Python binding of libfa.so (include/fa.h).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, then their device pointers and the current HIP stream go to the C ABI.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback path.  PyTorch supplies device memory and streams.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_F16, FA_BF16 = 0, 1
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
+SYMBOLS = ("fa_fwd", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_str")
+_DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load libfa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run exact_attention_22_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.fa_fwd.restype = i
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        L.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_fwd_splitkv.restype = i
+        L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.fa_splitkv_combine.restype = i
+        L.fa_splitkv_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.fa_status_str.restype = ctypes.c_char_p
+        L.fa_status_str.argtypes = [i]
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().fa_status_str(status).decode()
+
+
+def _check(status):
+    if status != FA_OK:
+        msg = status_str(status)
+        if status == FA_ERR_HIP:
+            raise FaError(status, msg)
+        raise ValueError(f"{msg} (status {status})")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_tensor(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _qkv(q, k, v):
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    ptrs = [_dev_tensor(t, n, q.dtype) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    return ptrs, (B, H, Nq, Nk, d)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """O, LSE of softmax(scale * Q K^T (+ causal mask)) V.  scale defaults to 1/sqrt(d)."""
+    (qp, kp, vp), (B, H, Nq, Nk, d) = _qkv(q, k, v)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("out must be [B, H, Nq, d] and lse [B, H, Nq]")
+    op = _dev_tensor(out, "out", q.dtype)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    _check(lib().fa_fwd(qp, kp, vp, op, lp, B, H, Nq, Nk, d, int(bool(causal)), _scale(scale, d),
+                        _DTYPES[q.dtype], _stream(stream)))
+    return out, lse
+
+
+def workspace_bytes(B, H, Nq, d, num_splits):
+    return int(lib().fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits))
+
+
+def fwd_splitkv(q, k, v, num_splits, causal=False, scale=None, o_part=None, lse_part=None, stream=None):
+    """Per-split normalised partials: o_part [S,B,H,Nq,d] fp32, lse_part [S,B,H,Nq] fp32."""
+    (qp, kp, vp), (B, H, Nq, Nk, d) = _qkv(q, k, v)
+    S = int(num_splits)
+    if o_part is None:
+        o_part = torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device)
+    if tuple(o_part.shape) != (S, B, H, Nq, d) or tuple(lse_part.shape) != (S, B, H, Nq):
+        raise ValueError("o_part must be [S, B, H, Nq, d] and lse_part [S, B, H, Nq]")
+    opp = _dev_tensor(o_part, "o_part", torch.float32)
+    lpp = _dev_tensor(lse_part, "lse_part", torch.float32)
+    _check(lib().fa_fwd_splitkv(qp, kp, vp, opp, lpp, B, H, Nq, Nk, d, int(bool(causal)),
+                                _scale(scale, d), S, _DTYPES[q.dtype], _stream(stream)))
+    return o_part, lse_part
+
+
+def splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, stream=None):
+    """Merge split partials into O (dtype) and LSE (fp32)."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float16 or bfloat16, got {dtype}")
+    if o_part.dim() != 5 or tuple(lse_part.shape) != tuple(o_part.shape[:4]):
+        raise ValueError("o_part must be [S, B, H, Nq, d] and lse_part [S, B, H, Nq]")
+    S, B, H, Nq, d = o_part.shape
+    opp = _dev_tensor(o_part, "o_part", torch.float32)
+    lpp = _dev_tensor(lse_part, "lse_part", torch.float32)
+    out = torch.empty((B, H, Nq, d), dtype=dtype, device=o_part.device) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_part.device) if lse is None else lse
+    if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("out must be [B, H, Nq, d] and lse [B, H, Nq]")
+    op = _dev_tensor(out, "out", dtype)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    _check(lib().fa_splitkv_combine(opp, lpp, op, lp, B, H, Nq, d, S, _DTYPES[dtype], _stream(stream)))
+    return out, lse
+
+
+def decode(q, k, v, num_splits=16, causal=False, scale=None, stream=None, o_part=None, lse_part=None):
+    """Split-KV forward followed by the combine, both on the same stream."""
+    o_part, lse_part = fwd_splitkv(q, k, v, num_splits, causal, scale, o_part, lse_part, stream)
+    return splitkv_combine(o_part, lse_part, q.dtype, stream=stream)

@@ -1,0 +1,113 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library, libfa.so.
+ *
+ * The library computes, for every batch b, head h and query row i,
+ *
+ *   O[b,h,i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:]  (+ causal mask) ) V[b,h,j,:]
+ *   LSE[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,h,j,:] )   over visible j
+ *
+ * tile by tile, without materialising the Nq x Nk score matrix.  Sources:
+ *   - Ringi, "Lecture 25: FlashAttention principles and Triton practice",
+ *     section 1.1 (three-step attention), section 2 (online softmax and the
+ *     rescaled output accumulator), experiment 3 (forward with LSE, default
+ *     scale 1/sqrt(d)).
+ *   - AIInfraGuide 6.2, "FlashAttention V2 explained", section 2 (Q outer, KV
+ *     inner), section 5 (causal block skipping) and its forward pseudocode
+ *     (saved statistic L = m + log l).
+ *   - LLM Infra Atlas, "FA2: parallelism and work partitioning", section 2
+ *     (grid over query tiles x batch x heads; split-KV with a combine kernel for
+ *     decode) and section 4 (causal key bound offset by seqlen_k - seqlen_q).
+ *   - KingOfEgg, "Flash Attention (4): v2.1 forward vs official source",
+ *     section 3.5 (inv_sum = 1 when the row sum is 0 or NaN; lse =
+ *     row_max * scale + log(sum)).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, contiguous, row-major: q and o are [B, H, Nq, d];
+ *     k and v are [B, H, Nk, d]; lse is float32 [B, H, Nq].  d is innermost.
+ *   - q, k, v and o hold the same 16-bit type (dtype).  All device pointers must
+ *     be 16-byte aligned.
+ *   - Causal visibility is bottom-right aligned: key j is visible to query i iff
+ *     j <= i + (Nk - Nq).  With Nq == Nk this is j <= i.  A query that sees no key
+ *     (only possible when causal and Nq > Nk) gets O = 0 and LSE = -inf.
+ *   - LSE is the natural log-sum-exp of the *scaled* scores.
+ *   - scale is used as given (any finite float; negative and zero allowed).
+ *   - Outputs are rounded to nearest even into dtype.
+ *   - Ownership: the caller owns every buffer.  The library allocates, frees and
+ *     synchronises nothing; all work is enqueued on `stream` (a hipStream_t;
+ *     NULL is the default stream) and returns before it completes.
+ *   - Errors: every argument is validated before any HIP call, so a bad call
+ *     returns without touching the device.  A kernel-launch failure reported by
+ *     the HIP runtime returns FA_ERR_HIP.  Nothing prints, aborts or throws.
+ *   - The results are deterministic: no atomics, fixed reduction orders.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,       /* B, H, Nq, Nk < 1, num_splits out of [1, Nk], or a size overflows */
+    FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite scale, misaligned pointer */
+    FA_ERR_WORKSPACE = 4,   /* reserved: a workspace too small for the request */
+    FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Prefill / full forward.  Writes o ([B,H,Nq,d], dtype) and lse ([B,H,Nq], fp32).
+ * One workgroup per (query tile, b, h) walks the key tiles that the causal bound
+ * leaves visible (LLM Infra Atlas, FA2 parallelism, sections 2 and 4).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * Bytes of partial results fa_fwd_splitkv writes for the given shape:
+ * num_splits * B * H * Nq * (d + 1) * 4.  Returns 0 for invalid sizes.
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
+
+/*
+ * Split-KV forward, first half (LLM Infra Atlas, FA2 parallelism, section 2:
+ * when seqlen_q is small, split the keys into num_splits chunks, each producing
+ * a partial (O, LSE)).  Split s covers keys [s*c, min(Nk, (s+1)*c)) with
+ * c = ceil(Nk / num_splits); trailing splits may be empty.  For every split and
+ * row it writes the attention restricted to that chunk, *normalised*, in fp32:
+ *   o_part   [num_splits, B, H, Nq, d]  float32
+ *   lse_part [num_splits, B, H, Nq]     float32  (-inf, with o_part = 0, when the
+ *                                                  row sees no key of the chunk)
+ * Causal visibility is applied inside each chunk.  1 <= num_splits <= Nk.
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v,
+                         float* o_part, float* lse_part,
+                         int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                         int num_splits, fa_dtype dtype, void* stream);
+
+/*
+ * Split-KV forward, second half: merge the partials with the online-softmax
+ * identity (Ringi, Lecture 25, section 2.2).  Per row:
+ *   M = max_s lse_part[s];  w_s = exp(lse_part[s] - M) (0 for -inf);
+ *   o = sum_s w_s o_part[s] / sum_s w_s  (rounded to dtype);
+ *   lse = M + ln sum_s w_s  (-inf, with o = 0, when every split is empty).
+ * Splits are summed in index order, so the result is deterministic.
+ */
+fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                             int B, int H, int Nq, int d, int num_splits,
+                             fa_dtype dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_str(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

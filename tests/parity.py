@@ -1,0 +1,46 @@
+"""Comparison of the HIP library's outputs with the fp64 oracle.
+
+Tolerances (the spec contract for this path): O max-abs 2e-3 for fp16 and
+1e-2 for bf16 outputs; LSE max |dLSE| / max(1, |LSE|) <= 1e-4.  Rows the oracle
+marks empty (LSE = -inf) must be exactly -inf with O exactly 0; NaN fails.
+"""
+import numpy as np
+import torch
+
+O_TOL = {torch.float16: 2e-3, torch.bfloat16: 1e-2, torch.float32: 2e-5}
+LSE_TOL = 1e-4
+
+
+def errors(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype):
+    o = o_gpu.detach().double().cpu().numpy().reshape(o_ref.shape)
+    l = lse_gpu.detach().double().cpu().numpy().reshape(lse_ref.shape)
+    assert not np.isnan(o).any(), "NaN in O"
+    assert not np.isnan(l).any(), "NaN in LSE"
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(l), empty), "empty rows differ"
+    assert np.all(o[empty] == 0.0), "empty rows must have O = 0"
+    fin = ~empty
+    o_err = float(np.max(np.abs(o - o_ref), initial=0.0))
+    lse_err = float(np.max(np.abs(l[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin])), initial=0.0))
+    ref_rounded = torch.from_numpy(np.ascontiguousarray(o_ref)).to(out_dtype).double().numpy()
+    o_err_rounded = float(np.max(np.abs(o - ref_rounded), initial=0.0))
+    return {"o_err": o_err, "lse_err": lse_err, "o_err_vs_rounded_oracle": o_err_rounded}
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype, what=""):
+    e = errors(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype)
+    print(f"[parity] {what} {e}", flush=True)
+    assert e["o_err"] <= O_TOL[out_dtype], f"{what}: O error {e}"
+    assert e["lse_err"] <= LSE_TOL, f"{what}: LSE error {e}"
+    return e
+
+
+def sample_rows(B, H, Nq, n_random=256, seed=0):
+    """Flat row indices (b*H + h)*Nq + i: the first and last rows of every head
+    plus seeded random rows."""
+    rng = np.random.default_rng(seed)
+    bh = np.arange(B * H)
+    rows = [bh * Nq, bh * Nq + (Nq - 1), rng.integers(0, B * H * Nq, n_random)]
+    if Nq > 1:
+        rows.append(bh * Nq + 1)
+    return np.unique(np.concatenate(rows))

@@ -1,0 +1,176 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Small shapes (several tiles plus ragged tails) are compared on every output
+element; the five named workloads are compared at full size on sampled rows,
+through the same calls the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_22_amd import fa
+from exact_attention_22_amd.inputs import BY_NAME, WORKLOADS, make_partials, make_qkv
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+F16, BF16 = torch.float16, torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def rnd(shape, dtype, seed, mult=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * mult).to(dtype)
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+SMALL = [  # B, H, Nq, Nk, d, causal, dtype
+    (1, 1, 128, 128, 64, False, F16),
+    (1, 2, 129, 200, 64, False, F16),
+    (2, 1, 257, 257, 128, True, F16),
+    (1, 2, 300, 300, 128, True, BF16),
+    (1, 1, 1, 77, 128, False, F16),
+    (1, 1, 1, 1, 64, True, F16),
+    (1, 1, 17, 1, 64, False, BF16),
+    (1, 2, 100, 333, 128, True, F16),     # Nq < Nk: bottom-right diagonal
+    (1, 1, 333, 100, 64, True, BF16),     # Nq > Nk: leading rows see nothing
+    (1, 1, 127, 129, 64, True, F16),
+    (3, 2, 64, 65, 128, False, BF16),
+    (1, 1, 1000, 1000, 128, True, BF16),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:5])) + f"-c{int(c[5])}-{str(c[6])[-4:]}")
+def test_fwd_small(dev, oracle_lib, case):
+    B, H, Nq, Nk, d, causal, dt = case
+    q, k, v = rnd((B, H, Nq, d), dt, 1), rnd((B, H, Nk, d), dt, 2), rnd((B, H, Nk, d), dt, 3)
+    say(f"fa_fwd {case}")
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle_lib.attention(q, k, v, causal, 1 / math.sqrt(d))
+    parity.check(o, lse, ro, rl, dt, f"fwd {case}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+def test_fwd_scales(dev, oracle_lib, scale):
+    B, H, N, d = 1, 2, 130, 64
+    q, k, v = (rnd((B, H, N, d), F16, s) for s in (4, 5, 6))
+    for causal in (False, True):
+        say(f"fa_fwd scale={scale} causal={causal}")
+        o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        ro, rl = oracle_lib.attention(q, k, v, causal, scale)
+        parity.check(o, lse, ro, rl, F16, f"scale {scale} causal {causal}")
+
+
+def test_fwd_closed_forms(dev):
+    """Identical keys give the running mean of V; the first causal row is v_0."""
+    B, H, N, d = 1, 2, 200, 128
+    q = rnd((B, H, N, d), F16, 7)
+    k = rnd((B, H, 1, d), F16, 8).expand(B, H, N, d).contiguous()
+    v = rnd((B, H, N, d), F16, 9)
+    say("fa_fwd identical keys")
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=True)
+    torch.cuda.synchronize()
+    vd = v.double()
+    running_mean = vd.cumsum(2) / torch.arange(1, N + 1, dtype=torch.float64)[:, None]
+    assert (o.cpu().double() - running_mean).abs().max().item() <= 2e-3
+    s = (q.double() * k.double()).sum(-1) / math.sqrt(d)
+    exp_l = s + torch.log(torch.arange(1, N + 1, dtype=torch.float64))
+    assert ((lse.cpu().double() - exp_l).abs() / exp_l.abs().clamp(min=1)).max().item() <= 1e-4
+    assert torch.equal(o.cpu()[:, :, 0], v[:, :, 0]), "first causal row must be exactly v_0"
+
+
+def test_fwd_deterministic_and_in_bounds(dev):
+    B, H, Nq, Nk, d = 2, 2, 190, 190, 128
+    q, k, v = (rnd((B, H, n, d), BF16, s).to(dev) for n, s in ((Nq, 10), (Nk, 11), (Nk, 12)))
+    pad = 4096
+    o_buf = torch.full((B * H * Nq * d + pad,), 12345.0, dtype=BF16, device=dev)
+    l_buf = torch.full((B * H * Nq + pad,), 777.0, dtype=torch.float32, device=dev)
+    o = o_buf[: B * H * Nq * d].view(B, H, Nq, d)
+    l = l_buf[: B * H * Nq].view(B, H, Nq)
+    say("fa_fwd canary")
+    fa.fwd(q, k, v, causal=True, out=o, lse=l)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[B * H * Nq * d:] == 12345.0) and torch.all(l_buf[B * H * Nq:] == 777.0)
+    assert torch.equal(o, o2) and torch.equal(l, l2), "two runs differ"
+
+
+@pytest.mark.parametrize("w", [w for w in WORKLOADS if not w.splits], ids=lambda w: w.name)
+def test_workload_prefill(dev, oracle_lib, w):
+    say(f"workload {w.name} inputs")
+    q, k, v = make_qkv(w, device=dev)
+    say(f"workload {w.name} fa_fwd")
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = None if w.B * w.H * w.Nq <= 4096 else parity.sample_rows(w.B, w.H, w.Nq)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    ro, rl = oracle_lib.attention(qc, kc, vc, w.causal, w.scale, rows=rows)
+    if rows is None:
+        parity.check(o, lse, ro, rl, w.dtype, w.name)
+    else:
+        idx = torch.from_numpy(rows)
+        parity.check(o.reshape(-1, w.d).cpu()[idx], lse.reshape(-1).cpu()[idx], ro, rl, w.dtype,
+                     f"{w.name} ({len(rows)} sampled rows)")
+
+
+def test_workload_decode(dev, oracle_lib):
+    w = BY_NAME["decode"]
+    say("workload decode inputs")
+    q, k, v = make_qkv(w, device=dev)
+    say("workload decode fa_fwd_splitkv + combine")
+    o, lse = fa.decode(q, k, v, num_splits=w.splits, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    ro, rl = oracle_lib.attention(qc, kc, vc, w.causal, w.scale)
+    parity.check(o, lse, ro, rl, w.dtype, "decode (all rows)")
+
+
+SPLIT_CASES = [  # B, H, Nq, Nk, d, causal, dtype
+    (2, 2, 1, 1000, 128, False, F16),
+    (1, 2, 1, 333, 64, True, BF16),
+    (1, 1, 1, 20, 128, False, BF16),
+    (1, 2, 70, 300, 128, True, F16),
+    (1, 1, 129, 129, 64, False, BF16),
+    (1, 1, 40, 20, 64, True, F16),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "x".join(map(str, c[:5])) + f"-c{int(c[5])}")
+@pytest.mark.parametrize("S", [1, 2, 16, 17])
+def test_splitkv(dev, oracle_lib, case, S):
+    B, H, Nq, Nk, d, causal, dt = case
+    q, k, v = rnd((B, H, Nq, d), dt, 21), rnd((B, H, Nk, d), dt, 22), rnd((B, H, Nk, d), dt, 23)
+    scale = 1 / math.sqrt(d)
+    say(f"fa_fwd_splitkv {case} S={S}")
+    op, lp = fa.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), S, causal=causal)
+    say(f"fa_splitkv_combine {case} S={S}")
+    o, lse = fa.splitkv_combine(op, lp, dt)
+    torch.cuda.synchronize()
+    rop, rlp = oracle_lib.split_partials(q, k, v, causal, scale, S)
+    parity.check(op, lp, rop, rlp, dt, f"partials {case} S={S}")
+    ro, rl = oracle_lib.attention(q, k, v, causal, scale)
+    parity.check(o, lse, ro, rl, dt, f"split+combine {case} S={S}")
+
+
+@pytest.mark.parametrize("empty_every", [0, 3, 1])
+@pytest.mark.parametrize("d,dt", [(64, F16), (128, BF16)])
+def test_combine_alone(dev, oracle_lib, empty_every, d, dt):
+    S, B, H, Nq = 5, 2, 3, 7
+    op, lp = make_partials(S, B, H, Nq, d, seed=31, empty_every=empty_every)
+    say(f"fa_splitkv_combine partials S={S} d={d} empty_every={empty_every}")
+    o, lse = fa.splitkv_combine(op.to(dev), lp.to(dev), dt)
+    torch.cuda.synchronize()
+    ro, rl = oracle_lib.combine(op.double().numpy(), lp.double().numpy())
+    parity.check(o, lse, ro, rl, dt, f"combine alone d={d} empty_every={empty_every}")
