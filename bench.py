@@ -1,0 +1,217 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * prefill: fa_fwd on the long-context causal workload
+    (B=1, H=32, Nq=Nk=8192, d=128, bf16, N(0,1)*0.5), and
+  * decode: fa_fwd_splitkv + fa_splitkv_combine on the decode workload
+    (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits).
+`value` is the prefill throughput in TFLOP/s with FLOPs = 4*B*H*Nq*Nk*d, halved
+for causal (Ringi, "Lecture 25", experiment 4); decode is reported as HBM GB/s
+over the bytes the method must move (Q + K + V + O + LSE).
+
+Each kernel is timed with HIP events recorded on the stream it is launched on.
+The CPU baseline times the fp64 oracle on a bounded sample of prefill rows.
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_attention_22_amd import fa                          # noqa: E402
+from exact_attention_22_amd.inputs import BY_NAME, make_qkv     # noqa: E402
+
+METRIC = "attn fwd TFLOPS & % MFMA peak (fp16 d=128 causal N=8K); decode HBM GB/s"
+PEAK_TFLOPS = {torch.bfloat16: 2500.0, torch.float16: 2500.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+FWD_SOURCES = ["exact_attention_22_amd/csrc/fa_fwd.hip", "exact_attention_22_amd/csrc/fa_device.h"]
+DEC_SOURCES = ["exact_attention_22_amd/csrc/fa_decode.hip", "exact_attention_22_amd/csrc/fa_device.h"]
+
+
+def attn_flops(B, H, Nq, Nk, d, causal):
+    """4*B*H*Nq*Nk*d, halved for causal (the pages' TFLOPS convention)."""
+    f = 4.0 * B * H * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def attn_bytes(B, H, Nq, Nk, d, elem=2):
+    """Q + K + V + O (elem bytes each) + LSE (fp32): each tensor touched once."""
+    return elem * (2 * B * H * Nq * d + 2 * B * H * Nk * d) + 4 * B * H * Nq
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from profiles/traffic_<key>.txt, if taken on this source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_key}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(q, k, v, w, target_rows):
+    """Time the fp64 oracle on evenly spaced rows of the prefill workload."""
+    import numpy as np
+    from oracle import oracle
+    orc = oracle.get()
+    nthreads = oracle.default_threads()
+    total = w.B * w.H * w.Nq
+    rows = np.linspace(0, total - 1, num=min(target_rows, total)).astype(np.int64)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    t0 = time.perf_counter()
+    orc.attention(qc, kc, vc, w.causal, w.scale, rows=rows, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    i = rows % w.Nq
+    visible = np.minimum(w.Nk, i + (w.Nk - w.Nq) + 1) if w.causal else np.full_like(i, w.Nk)
+    flops = float(np.sum(visible)) * w.d * 4.0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced query rows of {w.name} (of {total}); "
+                      f"{flops / 1e9:.1f} GFLOP of visible work in {dt:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=40000)
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also copy N MiB once (a plain copy of known size for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    fa.lib()
+
+    wp, wd = BY_NAME["long_causal"], BY_NAME["decode"]
+    do_p, do_d = args.only in ("all", "prefill"), args.only in ("all", "decode")
+    if do_p:
+        q, k, v = make_qkv(wp, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device=dev)
+    if do_d:
+        dq, dk, dv = make_qkv(wd, device=dev)
+        S = wd.splits
+        op = torch.empty((S, wd.B, wd.H, wd.Nq, wd.d), dtype=torch.float32, device=dev)
+        lp = torch.empty((S, wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+        do_ = torch.empty_like(dq)
+        dlse = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(rec):
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        if do_p:
+            fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse, stream=stream)
+        e[1].record(stream)
+        if do_d:
+            fa.fwd_splitkv(dq, dk, dv, S, causal=wd.causal, scale=wd.scale, o_part=op, lse_part=lp,
+                           stream=stream)
+        e[2].record(stream)
+        if do_d:
+            fa.splitkv_combine(op, lp, wd.dtype, out=do_, lse=dlse, stream=stream)
+        e[3].record(stream)
+        if rec is not None:
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def avg_ms(i, j):
+        return sum(r[i].elapsed_time(r[j]) for r in recs) / len(recs)
+
+    t_fwd, t_split, t_comb = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3)
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "data": "synthetic"}
+    cfg = {}
+    if do_p:
+        fl = attn_flops(wp.B, wp.H, wp.Nq, wp.Nk, wp.d, wp.causal)
+        tflops = fl / (t_fwd * 1e-3) / 1e12
+        src = source_hash(FWD_SOURCES)
+        out.update({"value": tflops, "unit": "TFLOP/s", "dtype": "bf16",
+                    "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wp.dtype]})
+        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[wp.dtype],
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_TFLOPS[wp.dtype],
+                           "traffic": read_traffic("fwd_long_causal", src),
+                           "kernel": "fwd_kernel<bf16, d=128, causal>", "avg_us": t_fwd * 1e3,
+                           "flop_per_launch": fl, "source_hash": src}
+        cfg["workload"] = ("long_causal: B=1 H=32 Nq=Nk=8192 d=128 bf16 causal (prefill, timed as value) + "
+                           "decode: B=8 H=32 Nq=1 Nk=32768 d=128 fp16 16 splits")
+        cfg.update({"prefill": {"B": wp.B, "H": wp.H, "Nq": wp.Nq, "Nk": wp.Nk, "d": wp.d,
+                                "dtype": "bf16", "causal": True, "input_scale": wp.mult}})
+    if do_d:
+        byts = attn_bytes(wd.B, wd.H, wd.Nq, wd.Nk, wd.d)
+        t_dec = t_split + t_comb
+        out["decode"] = {"GB_per_s": byts / (t_dec * 1e-3) / 1e9, "hbm_frac": byts / (t_dec * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "us_total": t_dec * 1e3, "us_splitkv": t_split * 1e3, "us_combine": t_comb * 1e3,
+                         "algorithmic_bytes": byts,
+                         "partials_bytes": fa.workspace_bytes(wd.B, wd.H, wd.Nq, wd.d, S)}
+        split_bytes = byts - 2 * wd.B * wd.H * wd.d - 4 * wd.B * wd.H   # O and LSE are the combine's
+        out["roofline_decode"] = {"bound": "hbm", "achieved": split_bytes / (t_split * 1e-3) / 1e9,
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": split_bytes / (t_split * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                  "traffic": read_traffic("decode", source_hash(DEC_SOURCES)),
+                                  "kernel": "decode_kernel<fp16, d=128>"}
+        if not do_p:
+            out.update({"value": out["decode"]["GB_per_s"], "unit": "GB/s", "dtype": "f16"})
+            cfg["workload"] = "decode: B=8 H=32 Nq=1 Nk=32768 d=128 fp16 16 splits"
+        cfg["decode"] = {"B": wd.B, "H": wd.H, "Nq": wd.Nq, "Nk": wd.Nk, "d": wd.d, "dtype": "fp16",
+                         "splits": S}
+    out["config"] = cfg
+    if do_p and not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(q, k, v, wp, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -99,4 +99,20 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
 }
 
+// Raw buffer resource (stride 0) over `bytes` bytes at `base`; loads at
+// offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, u32 bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// buffer_load_dwordx4 ... lds: every lane fetches the 16 bytes at byte offset
+// voff of the buffer, and the wave's 64 results land contiguously in LDS,
+// lane i at lds + 16*i (lds must be wave-uniform).  The caller waits for
+// completion (s_waitcnt vmcnt(0)) before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds, u32 voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds,
+                                             16, voff, 0, 0, 0);
+}
+
 }  // namespace fa

@@ -43,6 +43,8 @@
 //     true maximum keeps every P <= 256, well inside fp16 range.
 //   * Workgroups are ordered heaviest causal tile first and mapped so that
 //     consecutive tiles of one head share an XCD (and its L2).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -75,12 +77,13 @@ __device__ __forceinline__ int perm_row(int i) {
 template <bool BF16, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     constexpr int ROWB = D * 2;                  // bytes per K/V row
-    constexpr int CHUNKS = D / 8;                // 16-byte chunks per row
     constexpr int TILE = BC * ROWB;              // bytes per K (or V) tile
     constexpr int NS = D / 16;                   // 16-wide d slices of Q
     constexpr int ND = D / 32;                   // 32-wide d blocks of O^T
-    constexpr int LOADS = TILE / (256 * 16);     // 16-byte loads per thread per tensor per tile
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * TILE];
+    // two LDS stages, each [K tile | V tile]; separate objects so the compiler
+    // can tell a stage being filled from the one being read
+    __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
     // ---- work item -------------------------------------------------------
     const int total = gridDim.x;
@@ -126,32 +129,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
     }
 
-    // ---- K/V staging: global -> registers -> LDS ----------------------------
-    u32x4 kr[LOADS], vr[LOADS];
-    auto gload = [&](int tile) {
+    // ---- K/V tiles: buffer loads straight into LDS ---------------------------
+    // One wave instruction fills 1 KiB of LDS, lane i landing at byte 16*i.  Lane
+    // i therefore fetches the global chunk that the swizzled layout stores at
+    // that position; these offsets do not change from tile to tile.  Reads past
+    // the head's last key return zeros (the descriptor's record count).
+    constexpr int NPW = TILE / 1024 / 4;         // 1 KiB loads per wave per tensor per tile
+    u32 voff[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+        const int pos = (w * NPW + u) * 1024 + lane * 16;
+        const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
+        voff[u] = (u32)(row * ROWB + ((pchunk ^ swz<D>(row)) << 4));
+    }
+    auto load_tile = [&](int tile, unsigned char* stage) {
         const int k0 = ks + tile * BC;
+        const u32 nrec = (u32)(a.Nk - k0) * ROWB;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + (size_t)k0 * D, nrec);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + (size_t)k0 * D, nrec);
+        unsigned char* kb = stage + w * NPW * 1024;
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-            const int idx = tid + 256 * u;
-            const int r = idx / CHUNKS, c = idx % CHUNKS;
-            const int key = k0 + r;
-            if (key < ke) {
-                kr[u] = *(const u32x4*)(kg + (size_t)key * D + 8 * c);
-                vr[u] = *(const u32x4*)(vg + (size_t)key * D + 8 * c);
-            } else {
-                kr[u] = u32x4{0, 0, 0, 0};
-                vr[u] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-        unsigned char* kb = smem + buf * 2 * TILE;
-#pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-            const int idx = tid + 256 * u;
-            const int o = lds_off<D>(idx / CHUNKS, idx % CHUNKS);
-            *(u32x4*)(kb + o) = kr[u];
-            *(u32x4*)(kb + TILE + o) = vr[u];
+        for (int u = 0; u < NPW; ++u) {
+            lds_dma16(rk, kb + u * 1024, voff[u]);
+            lds_dma16(rv, kb + TILE + u * 1024, voff[u]);
         }
     };
 
@@ -161,31 +161,39 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     float Mu = -INFINITY;   // exponent reference (log2 units of scaled scores)
     float lsum = 0.f;       // this lane's half of the row sum, relative to Mu
 
-    const int krow0 = perm_row(l32);         // K row this lane feeds to S^T (within a 32-key block)
-    const int r4 = (lane & 15) >> 2;         // transpose-read row within a 4-row group
-    const int c4 = lane & 3;
-    const int g1 = (lane >> 4) & 1;
+    // per-lane LDS byte offsets of the operand reads (rows differing in bits
+    // 4-5 share a swizzle, so the 32-key block and 16-key group only add constants)
+    const int krow0 = perm_row(l32);             // K row fed to S^T within a 32-key block
+    int koff[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = lds_off<D>(krow0, 2 * s + h);
+    const int r4 = (lane & 15) >> 2, c4 = lane & 3, g1 = (lane >> 4) & 1;
+    int voffs[2][ND];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+            voffs[half][db] = lds_off<D>(8 * h + r4 + 4 * half, 4 * db + 2 * g1 + (c4 >> 1)) + (c4 & 1) * 8;
 
     // One key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
-    // need_mask (wave-uniform) is set only for tiles that cross the chunk end
-    // or, for causal attention, the diagonal.
-    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, bool need_mask) {
+    // MASKED tiles cross the chunk end or (causal) the diagonal.
+    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             sacc[kb] = f32x16{};
-            const int row = 32 * kb + krow0;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const u32x4 kf = *(const u32x4*)(Kb + lds_off<D>(row, 2 * s + h));
+                const u32x4 kf = *(const u32x4*)(Kb + 32 * kb * ROWB + koff[s]);
                 sacc[kb] = mfma32<BF16>(kf, qf[s], sacc[kb]);
             }
         }
-        // register r of block kb holds key k0 + 8h + kofs(kb, r); it is visible
-        // iff kofs < bound (the chunk end and, for causal, the diagonal)
-        int bound = ke - k0 - 8 * h;
-        if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
-        if (need_mask) {
+        // register r of block kb holds key k0 + 8h + kofs(kb, r); visible iff kofs < bound
+        int bound = 0;
+        if constexpr (MASKED) {
+            bound = ke - k0 - 8 * h;
+            if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -209,18 +217,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             Mu = Mn;
         }
         const float Mg = (Mu == -INFINITY) ? 0.f : Mu;   // no -inf - -inf
-        // P = 2^(s*c - M)
+        // P = 2^(s*c - M); masked keys weigh exactly 0 (also when scale is 0)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
-        if (need_mask) {   // masked keys weigh exactly 0, also when scale is 0
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = 0.f;
-        }
+            for (int r = 0; r < 16; ++r) {
+                float p = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
+                if constexpr (MASKED)
+                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) p = 0.f;
+                sacc[kb][r] = p;
+            }
         // row sum in fp32, before P is rounded to 16 bits
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -234,41 +240,59 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 const f32x16& P = sacc[kb];
                 const u32x4 pb = {pack2<BF16>(P[8 * p + 0], P[8 * p + 1]), pack2<BF16>(P[8 * p + 2], P[8 * p + 3]),
                                   pack2<BF16>(P[8 * p + 4], P[8 * p + 5]), pack2<BF16>(P[8 * p + 6], P[8 * p + 7])};
-                const int row = 32 * kb + 16 * p + 8 * h + r4;
+                const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) {
-                    const int chunk = 4 * db + 2 * g1 + (c4 >> 1);
-                    const int bo = (c4 & 1) * 8;
-                    const i16x4 lo = lds_read_tr16(Vb + lds_off<D>(row, chunk) + bo);
-                    const i16x4 hi4 = lds_read_tr16(Vb + lds_off<D>(row + 4, chunk) + bo);
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
                     const u32x4 va = {l2[0], l2[1], h2[0], h2[1]};
                     oacc[db] = mfma32<BF16>(va, pb, oacc[db]);
                 }
             }
     };
 
-    if (n_tiles > 0) {
-        gload(n_tiles - 1);
-        sstore(0);
+    // Tiles are walked from the last one down.  The first n_masked of them may
+    // cross the key-chunk end or the causal diagonal for some wave; all later
+    // ones are fully visible to every row of the workgroup.
+    int n_masked = 0;
+    while (n_masked < n_tiles) {
+        const int k0 = ks + (n_tiles - 1 - n_masked) * BC;
+        const bool clean = k0 + BC <= ke && (!CAUSAL || k0 + BC - 1 <= q0 + off);
+        if (clean) break;
+        ++n_masked;
     }
-    __syncthreads();
     const int qmax_w = min(qw + 31, a.Nq - 1);
+    if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // masked tiles: per-wave visibility checks, stage chosen at run time
+    int it = 0;
 #pragma clang loop unroll(disable)
-    for (int it = 0; it < n_tiles; ++it) {
+    for (; it < n_masked; ++it) {
         const int tile = n_tiles - 1 - it;
-        const int buf = it & 1;
-        if (it + 1 < n_tiles) gload(tile - 1);
+        unsigned char* cur = (it & 1) ? stage1 : stage0;
+        unsigned char* nxt = (it & 1) ? stage0 : stage1;
+        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
         const int k0 = ks + tile * BC;
         const bool active = qw < a.Nq && (!CAUSAL || k0 <= qmax_w + off);
-        if (active) {
-            const unsigned char* Kb = smem + buf * 2 * TILE;
-            const bool need_mask = (k0 + BC > ke) || (CAUSAL && k0 + BC - 1 > qw + off);
-            tile_step(Kb, Kb + TILE, k0, need_mask);
-        }
-        if (it + 1 < n_tiles) sstore(buf ^ 1);
+        if (active) tile_step(cur, cur + TILE, k0, std::true_type{});
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    }
+    // clean tiles, two per trip so that each half reads one fixed stage
+    auto clean_step = [&](unsigned char* cur, unsigned char* nxt) {
+        const int tile = n_tiles - 1 - it;
+        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+        tile_step(cur, cur + TILE, ks + tile * BC, std::false_type{});
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        ++it;
+    };
+    if ((it & 1) && it < n_tiles) clean_step(stage1, stage0);
+#pragma clang loop unroll(disable)
+    while (it < n_tiles) {
+        clean_step(stage0, stage1);
+        if (it < n_tiles) clean_step(stage1, stage0);
     }
 
     // ---- epilogue -------------------------------------------------------------
