@@ -35,7 +35,8 @@
 //     so the rescale by alpha is a per-lane multiply.
 //   * V stays row-major in LDS and ds_read_b64_tr_b16 produces the key-major
 //     operand.  K and V tiles are double-buffered in LDS through 16-byte
-//     coalesced global loads and an XOR swizzle (fa_device.h).
+//     coalesced buffer loads that write LDS directly and an XOR swizzle
+//     (fa_device.h).
 //   * Lazy rescale: the exponent reference only moves (and O, l are only
 //     rescaled) when a row's new maximum exceeds it by more than 2^8 in
 //     probability, decided per wavefront.  Any reference gives the same
@@ -142,17 +143,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
         voff[u] = (u32)(row * ROWB + ((pchunk ^ swz<D>(row)) << 4));
     }
-    auto load_tile = [&](int tile, unsigned char* stage) {
+    // which = 0 loads the K tile of `tile` into the stage, 1 its V tile
+    auto load_half = [&](int tile, unsigned char* stage, int which) {
         const int k0 = ks + tile * BC;
         const u32 nrec = (u32)(a.Nk - k0) * ROWB;
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + (size_t)k0 * D, nrec);
-        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + (size_t)k0 * D, nrec);
-        unsigned char* kb = stage + w * NPW * 1024;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * D, nrec);
+        unsigned char* dst = stage + which * TILE + w * NPW * 1024;
 #pragma unroll
-        for (int u = 0; u < NPW; ++u) {
-            lds_dma16(rk, kb + u * 1024, voff[u]);
-            lds_dma16(rv, kb + TILE + u * 1024, voff[u]);
-        }
+        for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
+    };
+    auto load_tile = [&](int tile, unsigned char* stage) {
+        load_half(tile, stage, 0);
+        load_half(tile, stage, 1);
     };
 
     f32x16 oacc[ND];
@@ -176,8 +178,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             voffs[half][db] = lds_off<D>(8 * h + r4 + 4 * half, 4 * db + 2 * g1 + (c4 >> 1)) + (c4 & 1) * 8;
 
     // One key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
-    // MASKED tiles cross the chunk end or (causal) the diagonal.
-    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag) {
+    // MASKED tiles cross the chunk end or (causal) the diagonal.  after_s runs
+    // once the S^T products are issued.
+    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag,
+                         auto&& after_s) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         f32x16 sacc[2];
 #pragma unroll
@@ -189,6 +193,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 sacc[kb] = mfma32<BF16>(kf, qf[s], sacc[kb]);
             }
         }
+        after_s();
         // register r of block kb holds key k0 + 8h + kofs(kb, r); visible iff kofs < bound
         int bound = 0;
         if constexpr (MASKED) {
@@ -275,15 +280,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
         const int k0 = ks + tile * BC;
         const bool active = qw < a.Nq && (!CAUSAL || k0 <= qmax_w + off);
-        if (active) tile_step(cur, cur + TILE, k0, std::true_type{});
+        if (active) tile_step(cur, cur + TILE, k0, std::true_type{}, [] {});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    // clean tiles, two per trip so that each half reads one fixed stage
+    // clean tiles, two per trip so that each half reads one fixed stage.  The
+    // next tile's K loads go out at the start of the step and its V loads after
+    // the S^T products: one burst of all of a workgroup's loads would queue in
+    // the CU's address unit and stall every wave at the step start.
     auto clean_step = [&](unsigned char* cur, unsigned char* nxt) {
         const int tile = n_tiles - 1 - it;
-        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
-        tile_step(cur, cur + TILE, ks + tile * BC, std::false_type{});
+        const bool more = it + 1 < n_tiles;
+        if (more) load_half(tile - 1, nxt, 0);
+        tile_step(cur, cur + TILE, ks + tile * BC, std::false_type{}, [&] {
+            if (more) load_half(tile - 1, nxt, 1);
+        });
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         ++it;
