@@ -83,13 +83,57 @@ typedef struct {
     int dtype, B, H, Nq, Nk, d, causal;
     double sigma;
     int key_begin, key_end;
-    const int64_t *rows;      /* flat (b*H + h)*Nq + i indices, or NULL for all rows */
+    const int64_t *rows;      /* flat (b*H + h)*Nq + i indices (varlen: token*H + h), or NULL */
     int64_t nrows;
     double *o, *lse;          /* o: [nrows, d], lse: [nrows] */
     int64_t first, last;      /* this worker's slice of [0, nrows) */
+    /* packed variable-length layout (varlen != 0) */
+    int varlen, H_kv, total_q, max_k;
+    const int32_t *cu_q, *cu_k;
 } job_t;
 
-/* One query row, written straight from the definition above. */
+/*
+ * One query row against keys lo <= j < hi, written straight from the definition
+ * above.  qp is the query row; kp and vp point at key 0 of the row's key/value
+ * sequence, whose rows are kstride elements apart.
+ */
+static void row_core(const uint16_t *qp, const uint16_t *kp, const uint16_t *vp, size_t kstride,
+                     int d, int lo, int hi, int dtype, double sigma,
+                     double *o_row, double *lse_out, double *qrow, double *s) {
+    for (int t = 0; t < d; ++t) o_row[t] = 0.0;
+    if (hi <= lo) { *lse_out = -INFINITY; return; }
+
+    for (int t = 0; t < d; ++t) qrow[t] = decode(qp[t], dtype);
+
+    /* scores of the visible keys and their maximum */
+    double m = -INFINITY;
+    for (int j = lo; j < hi; ++j) {
+        double acc = 0.0;
+        const uint16_t *kj = kp + (size_t)j * kstride;
+        for (int t = 0; t < d; ++t) acc += qrow[t] * decode(kj[t], dtype);
+        s[j - lo] = sigma * acc;
+        if (s[j - lo] > m) m = s[j - lo];
+    }
+    /* softmax denominator and weighted sum of V */
+    double l = 0.0;
+    for (int j = lo; j < hi; ++j) {
+        double p = exp(s[j - lo] - m);
+        l += p;
+        const uint16_t *vj = vp + (size_t)j * kstride;
+        for (int t = 0; t < d; ++t) o_row[t] += p * decode(vj[t], dtype);
+    }
+    for (int t = 0; t < d; ++t) o_row[t] /= l;
+    *lse_out = m + log(l);
+}
+
+/* Last visible key + 1 for query i of a sequence of Nq queries and Nk keys. */
+static int causal_end(int i, int Nq, int Nk, int lo, int hi) {
+    int64_t lim = (int64_t)i + (Nk - Nq) + 1;              /* keys j <= i + Nk - Nq */
+    if (lim < hi) hi = lim < lo ? lo : (int)lim;
+    return hi;
+}
+
+/* One row of the [B, H, N, d] layout. */
 static void one_row(const job_t *jb, int64_t flat, double *o_row, double *lse_out,
                     double *qrow, double *s) {
     const int d = jb->d, Nq = jb->Nq, Nk = jb->Nk;
@@ -101,49 +145,57 @@ static void one_row(const job_t *jb, int64_t flat, double *o_row, double *lse_ou
 
     int lo = jb->key_begin < 0 ? 0 : jb->key_begin;
     int hi = jb->key_end > Nk ? Nk : jb->key_end;
-    if (jb->causal) {
-        int64_t lim = (int64_t)i + (Nk - Nq) + 1;          /* keys j <= i + Nk - Nq */
-        if (lim < hi) hi = lim < lo ? lo : (int)lim;
-    }
-    for (int t = 0; t < d; ++t) o_row[t] = 0.0;
-    if (hi <= lo) { *lse_out = -INFINITY; return; }
+    if (jb->causal) hi = causal_end(i, Nq, Nk, lo, hi);
+    row_core(qp, kp, vp, (size_t)d, d, lo, hi, jb->dtype, jb->sigma, o_row, lse_out, qrow, s);
+}
 
-    for (int t = 0; t < d; ++t) qrow[t] = decode(qp[t], jb->dtype);
-
-    /* scores of the visible keys and their maximum */
-    double m = -INFINITY;
-    for (int j = lo; j < hi; ++j) {
-        double acc = 0.0;
-        const uint16_t *kj = kp + (size_t)j * d;
-        for (int t = 0; t < d; ++t) acc += qrow[t] * decode(kj[t], jb->dtype);
-        s[j - lo] = jb->sigma * acc;
-        if (s[j - lo] > m) m = s[j - lo];
-    }
-    /* softmax denominator and weighted sum of V */
-    double l = 0.0;
-    for (int j = lo; j < hi; ++j) {
-        double p = exp(s[j - lo] - m);
-        l += p;
-        const uint16_t *vj = vp + (size_t)j * d;
-        for (int t = 0; t < d; ++t) o_row[t] += p * decode(vj[t], jb->dtype);
-    }
-    for (int t = 0; t < d; ++t) o_row[t] /= l;
-    *lse_out = m + log(l);
+/*
+ * One row of the packed variable-length layout with grouped K/V heads
+ * (KingOfEgg, "Flash Attention (4)", section 5: K/V indexed by head group and
+ * sequences delimited by cumulative offsets cu_seqlens; Ringi, "Lecture 25",
+ * section 7: packing without padding).  q: [total_q, H, d]; k, v: [total_k,
+ * H_kv, d].  Sequence b owns query tokens [cu_q[b], cu_q[b+1]) and key tokens
+ * [cu_k[b], cu_k[b+1]); query head h reads K/V head h / (H / H_kv).  Within a
+ * sequence the definition above applies with its own Nq and Nk.
+ */
+static void varlen_row(const job_t *jb, int64_t flat, double *o_row, double *lse_out,
+                       double *qrow, double *s) {
+    const int d = jb->d, H = jb->H, H_kv = jb->H_kv;
+    const int64_t token = flat / H;
+    const int h = (int)(flat % H);
+    int b = 0;
+    while (b + 1 < jb->B && jb->cu_q[b + 1] <= token) ++b;  /* sequence holding the token */
+    const int i = (int)(token - jb->cu_q[b]);
+    const int Nq = jb->cu_q[b + 1] - jb->cu_q[b];
+    const int Nk = jb->cu_k[b + 1] - jb->cu_k[b];
+    const int g = h / (H / H_kv);
+    const uint16_t *qp = jb->q + ((size_t)token * H + h) * d;
+    const uint16_t *kp = jb->k + ((size_t)jb->cu_k[b] * H_kv + g) * d;
+    const uint16_t *vp = jb->v + ((size_t)jb->cu_k[b] * H_kv + g) * d;
+    int hi = Nk;
+    if (jb->causal) hi = causal_end(i, Nq, Nk, 0, hi);
+    row_core(qp, kp, vp, (size_t)H_kv * d, d, 0, hi, jb->dtype, jb->sigma, o_row, lse_out, qrow, s);
 }
 
 static void *worker(void *arg) {
     job_t *jb = (job_t *)arg;
+    const int max_k = jb->varlen ? jb->max_k : jb->Nk;
     double *qrow = (double *)malloc(sizeof(double) * (size_t)jb->d);
-    double *s = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
+    double *s = (double *)malloc(sizeof(double) * (size_t)(max_k > 0 ? max_k : 1));
     if (!qrow || !s) { free(qrow); free(s); return (void *)1; }
     for (int64_t r = jb->first; r < jb->last; ++r) {
         int64_t flat = jb->rows ? jb->rows[r] : r;
-        one_row(jb, flat, jb->o + r * jb->d, jb->lse + r, qrow, s);
+        if (jb->varlen)
+            varlen_row(jb, flat, jb->o + r * jb->d, jb->lse + r, qrow, s);
+        else
+            one_row(jb, flat, jb->o + r * jb->d, jb->lse + r, qrow, s);
     }
     free(qrow);
     free(s);
     return NULL;
 }
+
+static int run_jobs(const job_t *base, int nthreads);
 
 /*
  * Attention rows of [B, H, Nq, d] queries against [B, H, Nk, d] keys/values,
@@ -163,12 +215,48 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
     if (rows)
         for (int64_t r = 0; r < nrows; ++r)
             if (rows[r] < 0 || rows[r] >= total) return -1;
+    job_t base = {q, k, v, dtype, B, H, Nq, Nk, d, causal, (double)scale,
+                  key_begin, key_end, rows, nrows, o, lse, 0, 0, 0, H, 0, 0, NULL, NULL};
+    return run_jobs(&base, nthreads);
+}
+
+/*
+ * Attention rows of the packed layout (see varlen_row): rows == NULL means every
+ * (token, head) in flat order token*H + h (nrows must then be total_q*H); o is
+ * [nrows, d], lse [nrows].  cu_q and cu_k are host arrays of B+1 non-decreasing
+ * offsets starting at 0.  Returns 0, or -1 on a bad argument, -2 on allocation
+ * or thread failure.
+ */
+int oracle_attention_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
+                            int B, int H, int H_kv, int d, const int32_t *cu_q, const int32_t *cu_k,
+                            int causal, float scale, const int64_t *rows, int64_t nrows,
+                            double *o, double *lse, int nthreads) {
+    if (!q || !k || !v || !o || !lse || !cu_q || !cu_k) return -1;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || d <= 0 || nrows < 0) return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (cu_q[0] != 0 || cu_k[0] != 0) return -1;
+    int max_k = 0;
+    for (int b = 0; b < B; ++b) {
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
+        if (cu_k[b + 1] - cu_k[b] > max_k) max_k = cu_k[b + 1] - cu_k[b];
+    }
+    const int64_t total = (int64_t)cu_q[B] * H;
+    if (!rows && nrows != total) return -1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= total) return -1;
+    job_t base = {q, k, v, dtype, B, H, 0, 0, d, causal, (double)scale,
+                  0, 0, rows, nrows, o, lse, 0, 0, 1, H_kv, cu_q[B], max_k, cu_q, cu_k};
+    return run_jobs(&base, nthreads);
+}
+
+/* Split rows [0, base->nrows) over nthreads workers and run them. */
+static int run_jobs(const job_t *basep, int nthreads) {
+    const job_t base = *basep;
+    const int64_t nrows = base.nrows;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if ((int64_t)nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
-
-    job_t base = {q, k, v, dtype, B, H, Nq, Nk, d, causal, (double)scale,
-                  key_begin, key_end, rows, nrows, o, lse, 0, 0};
     job_t jobs[256];
     pthread_t tid[256];
     int started[256];

@@ -21,6 +21,7 @@ _DTYPE_CODE = {torch.float16: 0, torch.bfloat16: 1}
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 def default_threads():
@@ -51,6 +52,11 @@ class Oracle:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_float, ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64,
             _f64p, _f64p, ctypes.c_int]
+        lib.oracle_attention_varlen.restype = ctypes.c_int
+        lib.oracle_attention_varlen.argtypes = [
+            _u16p, _u16p, _u16p, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p,
+            ctypes.c_int, ctypes.c_float, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_combine.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                        _f64p, _f64p]
@@ -100,6 +106,47 @@ class Oracle:
             raise RuntimeError(f"oracle_attention_rows failed ({rc})")
         if rows is None:
             return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+        return o, lse
+
+    # -- packed variable-length sequences, grouped K/V heads -------------
+    def attention_varlen(self, q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, rows=None,
+                         nthreads=None):
+        """fp64 attention of packed sequences: q [total_q, H, d] against k, v
+        [total_k, H_kv, d], sequence b spanning tokens [cu[b], cu[b+1]) of each;
+        query head h reads K/V head h // (H // H_kv).
+
+        rows: optional flat indices token*H + h; then o is [len(rows), d] and lse
+        [len(rows)], otherwise o is [total_q, H, d] and lse [H, total_q].
+        """
+        if q.dtype != k.dtype or q.dtype != v.dtype:
+            raise TypeError("q, k, v must share a dtype")
+        total_q, H, d = q.shape
+        total_k, H_kv = k.shape[0], k.shape[1]
+        if tuple(k.shape) != (total_k, H_kv, d) or tuple(v.shape) != (total_k, H_kv, d):
+            raise ValueError("k and v must be [total_k, H_kv, d] matching q")
+        cq = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int32))
+        ck = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int32))
+        B = cq.size - 1
+        if ck.size != B + 1 or B < 1 or cq[-1] != total_q or ck[-1] != total_k:
+            raise ValueError("cu_seqlens must hold B+1 offsets ending at total_q / total_k")
+        qb, kb, vb = _bits(q), _bits(k), _bits(v)
+        if rows is None:
+            rows_arr = None
+            nrows = total_q * H
+        else:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            nrows = rows_arr.size
+        o = np.empty((nrows, d), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rc = self.lib.oracle_attention_varlen(
+            _ptr(qb, _u16p), _ptr(kb, _u16p), _ptr(vb, _u16p), _DTYPE_CODE[q.dtype],
+            B, H, H_kv, d, _ptr(cq, _i32p), _ptr(ck, _i32p), int(bool(causal)), float(scale),
+            _ptr(rows_arr, _i64p) if rows_arr is not None else None, nrows,
+            _ptr(o, _f64p), _ptr(lse, _f64p), nthreads or default_threads())
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_varlen failed ({rc})")
+        if rows is None:
+            return o.reshape(total_q, H, d), lse.reshape(total_q, H).T.copy()
         return o, lse
 
     # -- split-KV ---------------------------------------------------------

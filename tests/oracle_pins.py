@@ -302,7 +302,84 @@ def pin_worked_examples(orc):
             _close(lse, np.array([_eval(x) for x in ex["LSE"]]), 1e-14, ex["name"])
 
 
+# -- packed variable-length sequences with grouped K/V heads ---------------
+# KingOfEgg "Flash Attention (4)", section 5 (K/V indexed by head group, entry
+# with cu_seqlens); Ringi "Lecture 25", section 7 (packing without padding).
+
+def _packed(lens, heads, d, dt, seed):
+    """Random packed [sum(lens), heads, d] tensor and its cumulative offsets."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return _rand((int(cu[-1]), heads, d), dt, seed), cu
+
+
+VARLEN_CASES = [  # (q lens, k lens, H, d, causal)
+    ([5, 0, 9, 1], [7, 3, 9, 4], 2, 8, True),
+    ([5, 0, 9, 1], [7, 3, 9, 4], 2, 8, False),
+    ([12, 3], [4, 3], 3, 16, True),            # Nq > Nk: leading rows of sequence 0 see no key
+    ([6, 2, 7], [0, 5, 7], 1, 8, True),        # a sequence with no keys
+    ([1, 1, 1], [13, 2, 1], 2, 64, False),
+]
+
+
+def pin_varlen_per_sequence(orc):
+    """With H_kv = H each sequence of a packed batch equals the [B,H,N,d] oracle
+    (itself pinned above) on that sequence alone, rows and heads transposed."""
+    n = 0
+    for ql, kl, H, d, causal in VARLEN_CASES:
+        for dt in DTYPES:
+            q, cq = _packed(ql, H, d, dt, 700 + n)
+            k, ck = _packed(kl, H, d, dt, 800 + n)
+            v, _ = _packed(kl, H, d, dt, 900 + n)
+            n += 1
+            o, lse = orc.attention_varlen(q, k, v, cq, ck, causal, 0.3, nthreads=2)
+            assert o.shape == (int(cq[-1]), H, d) and lse.shape == (H, int(cq[-1])), "varlen shapes"
+            for b in range(len(ql)):
+                if ql[b] == 0:
+                    continue
+                sq = q[cq[b]:cq[b + 1]].permute(1, 0, 2)[None].contiguous()
+                if kl[b] == 0:
+                    _close(o[cq[b]:cq[b + 1]], np.zeros((ql[b], H, d)), 0.0, "no-key sequence O")
+                    assert np.all(lse[:, cq[b]:cq[b + 1]] == -np.inf), "no-key sequence LSE"
+                    continue
+                sk = k[ck[b]:ck[b + 1]].permute(1, 0, 2)[None].contiguous()
+                sv = v[ck[b]:ck[b + 1]].permute(1, 0, 2)[None].contiguous()
+                ro, rl = orc.attention(sq, sk, sv, causal, 0.3, nthreads=1)
+                _close(o[cq[b]:cq[b + 1]], ro[0].transpose(1, 0, 2), 1e-15, f"varlen seq {b} O")
+                _close(lse[:, cq[b]:cq[b + 1]], rl[0], 1e-15, f"varlen seq {b} LSE")
+
+
+def pin_varlen_grouped_heads(orc):
+    """Grouped K/V heads (H_kv < H, MQA at H_kv = 1) equal full multi-head attention
+    with each K/V head repeated for the H / H_kv consecutive query heads of its group."""
+    for H, H_kv in ((4, 2), (6, 3), (4, 1), (8, 4)):
+        for causal in (False, True):
+            ql, kl, d, dt = [9, 4, 0, 6], [9, 11, 2, 3], 8, torch.bfloat16
+            q, cq = _packed(ql, H, d, dt, 1000 + H * 10 + H_kv)
+            k, ck = _packed(kl, H_kv, d, dt, 1100 + H * 10 + H_kv)
+            v, _ = _packed(kl, H_kv, d, dt, 1200 + H * 10 + H_kv)
+            o, lse = orc.attention_varlen(q, k, v, cq, ck, causal, 0.45, nthreads=2)
+            G = H // H_kv
+            k_full = k.repeat_interleave(G, dim=1).contiguous()
+            v_full = v.repeat_interleave(G, dim=1).contiguous()
+            ro, rl = orc.attention_varlen(q, k_full, v_full, cq, ck, causal, 0.45, nthreads=2)
+            _close(o, ro, 0.0, f"grouped heads O H={H} H_kv={H_kv}")
+            _close(lse, rl, 0.0, f"grouped heads LSE H={H} H_kv={H_kv}")
+
+
+def pin_varlen_rows(orc):
+    """Selected rows (token*H + h) equal the same rows of the full result."""
+    ql, kl, H, d = [7, 5], [3, 9], 4, 16
+    q, cq = _packed(ql, H, d, torch.float16, 1301)
+    k, ck = _packed(kl, 2, d, torch.float16, 1302)
+    v, _ = _packed(kl, 2, d, torch.float16, 1303)
+    o, lse = orc.attention_varlen(q, k, v, cq, ck, True, 0.5, nthreads=1)
+    rows = np.array([0, 5, 13, 27, 47])
+    ro, rl = orc.attention_varlen(q, k, v, cq, ck, True, 0.5, rows=rows, nthreads=1)
+    _close(ro, o.reshape(-1, d)[rows], 0.0, "varlen selected rows O")
+    _close(rl, lse.T.reshape(-1)[rows], 0.0, "varlen selected rows LSE")
+
+
 ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
-            pin_worked_examples]
+            pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows]

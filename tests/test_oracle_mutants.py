@@ -10,7 +10,7 @@ from oracle import build, oracle
 from tests import oracle_pins
 
 MUTANTS = [
-    ("drop_scale", "s[j - lo] = jb->sigma * acc;", "s[j - lo] = acc;"),
+    ("drop_scale", "s[j - lo] = sigma * acc;", "s[j - lo] = acc;"),
     ("score_sign", "acc += qrow[t] * decode", "acc -= qrow[t] * decode"),
     ("causal_off_by_one", "(int64_t)i + (Nk - Nq) + 1;", "(int64_t)i + (Nk - Nq);"),
     ("causal_offset_sign", "(int64_t)i + (Nk - Nq) + 1;", "(int64_t)i - (Nk - Nq) + 1;"),
@@ -19,8 +19,8 @@ MUTANTS = [
     ("lse_without_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
     ("lse_without_log", "*lse_out = m + log(l);", "*lse_out = m + l;"),
     ("unnormalised_output", "for (int t = 0; t < d; ++t) o_row[t] /= l;", "for (int t = 0; t < d; ++t) o_row[t] /= 1.0;"),
-    ("k_row_stride", "const uint16_t *kj = kp + (size_t)j * d;", "const uint16_t *kj = kp + (size_t)j;"),
-    ("v_row_of_query", "const uint16_t *vj = vp + (size_t)j * d;", "const uint16_t *vj = vp + (size_t)i * d;"),
+    ("k_row_stride", "const uint16_t *kj = kp + (size_t)j * kstride;", "const uint16_t *kj = kp + (size_t)j;"),
+    ("v_row_of_first_key", "const uint16_t *vj = vp + (size_t)j * kstride;", "const uint16_t *vj = vp + (size_t)lo * kstride;"),
     ("q_row_of_key", "jb->q + ((size_t)bh * Nq + i) * d;", "jb->q + ((size_t)bh * Nq) * d;"),
     ("head_stride", "const uint16_t *kp = jb->k + (size_t)bh * Nk * d;", "const uint16_t *kp = jb->k;"),
     ("f16_exponent_bias", "expo - 25", "expo - 24"),
@@ -30,6 +30,17 @@ MUTANTS = [
     ("combine_weight_sign", "double w = exp(ls - M);", "double w = exp(M - ls);"),
     ("combine_lse_missing_max", "lse[r] = M + log(wsum);", "lse[r] = log(wsum);"),
     ("combine_skip_normalise", "for (int t = 0; t < d; ++t) orow[t] /= wsum;", "for (int t = 0; t < d; ++t) orow[t] /= 1.0;"),
+    ("varlen_group_modulo", "const int g = h / (H / H_kv);", "const int g = h % H_kv;"),
+    ("varlen_key_offset_of_queries", "const uint16_t *kp = jb->k + ((size_t)jb->cu_k[b] * H_kv + g) * d;",
+     "const uint16_t *kp = jb->k + ((size_t)jb->cu_q[b] * H_kv + g) * d;"),
+    ("varlen_value_head", "const uint16_t *vp = jb->v + ((size_t)jb->cu_k[b] * H_kv + g) * d;",
+     "const uint16_t *vp = jb->v + ((size_t)jb->cu_k[b] * H_kv) * d;"),
+    ("varlen_key_stride", "row_core(qp, kp, vp, (size_t)H_kv * d,", "row_core(qp, kp, vp, (size_t)d,"),
+    ("varlen_key_count", "const int Nk = jb->cu_k[b + 1] - jb->cu_k[b];", "const int Nk = jb->cu_q[b + 1] - jb->cu_q[b];"),
+    ("varlen_query_head", "const uint16_t *qp = jb->q + ((size_t)token * H + h) * d;",
+     "const uint16_t *qp = jb->q + ((size_t)token * H) * d;"),
+    ("varlen_sequence_search", "while (b + 1 < jb->B && jb->cu_q[b + 1] <= token) ++b;",
+     "while (b + 1 < jb->B && jb->cu_q[b + 1] < token) ++b;"),
     ("empty_row_lse_zero", "if (hi <= lo) { *lse_out = -INFINITY; return; }", "if (hi <= lo) { *lse_out = 0.0; return; }"),
 ]
 
@@ -42,7 +53,8 @@ def test_mutant_is_caught(tmp_path, name, old, new):
     mpath = os.path.join(tmp_path, f"{name}.c")
     with open(mpath, "w") as f:
         f.write(src.replace(old, new))
-    lib = build.build(src=mpath, out=os.path.join(tmp_path, f"lib{name}.so"))
+    # a mutant may leave a parameter unused: warnings stay warnings here
+    lib = build.build(src=mpath, out=os.path.join(tmp_path, f"lib{name}.so"), extra_flags=("-Wno-error",))
     orc = oracle.Oracle(lib)
     caught = []
     for pin in oracle_pins.ALL_PINS:
