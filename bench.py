@@ -4,10 +4,13 @@ One step = one pass of the whole path over resident synthetic inputs:
   * prefill: fa_fwd on the long-context causal workload
     (B=1, H=32, Nq=Nk=8192, d=128, bf16, N(0,1)*0.5), and
   * decode: fa_fwd_splitkv + fa_splitkv_combine on the decode workload
-    (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits).
+    (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits), and
+  * varlen: fa_fwd_varlen on 16 packed causal sequences (lengths log-uniform in
+    [64, 8192], 20752 tokens) with 32 query heads sharing 8 K/V heads, d=128, bf16.
 `value` is the prefill throughput in TFLOP/s with FLOPs = 4*B*H*Nq*Nk*d, halved
 for causal (Ringi, "Lecture 25", experiment 4); decode is reported as HBM GB/s
-over the bytes the method must move (Q + K + V + O + LSE).
+over the bytes the method must move (Q + K + V + O + LSE); varlen as TFLOP/s with
+the same FLOP convention summed over its sequences.
 
 Each kernel is timed with HIP events recorded on the stream it is launched on.
 The CPU baseline times the fp64 oracle on a bounded sample of prefill rows.
@@ -27,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_attention_22_amd import fa                          # noqa: E402
-from exact_attention_22_amd.inputs import BY_NAME, make_qkv     # noqa: E402
+from exact_attention_22_amd.inputs import BY_NAME, make_qkv, make_varlen     # noqa: E402
 
 METRIC = "attn fwd TFLOPS & % MFMA peak (fp16 d=128 causal N=8K); decode HBM GB/s"
 PEAK_TFLOPS = {torch.bfloat16: 2500.0, torch.float16: 2500.0}   # MI355X dense MFMA
@@ -100,7 +103,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=40000)
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -116,8 +119,9 @@ def main():
     dev = torch.device("cuda:0")
     fa.lib()
 
-    wp, wd = BY_NAME["long_causal"], BY_NAME["decode"]
+    wp, wd, wv = BY_NAME["long_causal"], BY_NAME["decode"], BY_NAME["varlen_gqa"]
     do_p, do_d = args.only in ("all", "prefill"), args.only in ("all", "decode")
+    do_v = args.only in ("all", "varlen")
     if do_p:
         q, k, v = make_qkv(wp, device=dev)
         o = torch.empty_like(q)
@@ -129,6 +133,11 @@ def main():
         lp = torch.empty((S, wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
         do_ = torch.empty_like(dq)
         dlse = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+    if do_v:
+        vq, vk, vv, vcq, vck = make_varlen(wv, device=dev)
+        vo = torch.empty_like(vq)
+        vlse = torch.empty((wv.H, vq.shape[0]), dtype=torch.float32, device=dev)
+        vmax = max(wv.seqlens)
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -141,7 +150,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e = [ev() for _ in range(4)]
+        e = [ev() for _ in range(5)]
         e[0].record(stream)
         if do_p:
             fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse, stream=stream)
@@ -153,6 +162,10 @@ def main():
         if do_d:
             fa.splitkv_combine(op, lp, wd.dtype, out=do_, lse=dlse, stream=stream)
         e[3].record(stream)
+        if do_v:
+            fa.fwd_varlen(vq, vk, vv, vcq, vck, vmax, vmax, causal=wv.causal, scale=wv.scale, out=vo,
+                          lse=vlse, stream=stream)
+        e[4].record(stream)
         if rec is not None:
             rec.append(e)
 
@@ -169,7 +182,7 @@ def main():
     def avg_ms(i, j):
         return sum(r[i].elapsed_time(r[j]) for r in recs) / len(recs)
 
-    t_fwd, t_split, t_comb = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3)
+    t_fwd, t_split, t_comb, t_var = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic"}
@@ -207,6 +220,20 @@ def main():
             cfg["workload"] = "decode: B=8 H=32 Nq=1 Nk=32768 d=128 fp16 16 splits"
         cfg["decode"] = {"B": wd.B, "H": wd.H, "Nq": wd.Nq, "Nk": wd.Nk, "d": wd.d, "dtype": "fp16",
                          "splits": S}
+    if do_v:
+        fl = sum(attn_flops(1, wv.H, n, n, wv.d, wv.causal) for n in wv.seqlens)
+        tf = fl / (t_var * 1e-3) / 1e12
+        out["varlen_gqa"] = {"TFLOP_per_s": tf, "pct_mfma_peak": 100.0 * tf / PEAK_TFLOPS[wv.dtype],
+                             "avg_us": t_var * 1e3, "flop_per_launch": fl}
+        out["roofline_varlen"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_TFLOPS[wv.dtype],
+                                  "unit": "TFLOP/s", "frac": tf / PEAK_TFLOPS[wv.dtype],
+                                  "traffic": read_traffic("fwd_varlen_gqa", source_hash(FWD_SOURCES)),
+                                  "kernel": "fwd_kernel<bf16, d=128, causal, varlen>"}
+        cfg["varlen"] = {"sequences": wv.B, "tokens": sum(wv.seqlens), "max_seqlen": max(wv.seqlens),
+                         "H": wv.H, "H_kv": wv.H_kv, "d": wv.d, "dtype": "bf16", "causal": True}
+        if not do_p and not do_d:
+            out.update({"value": tf, "unit": "TFLOP/s", "dtype": "bf16"})
+            cfg["workload"] = "varlen_gqa: 16 packed causal sequences, 20752 tokens, H=32 H_kv=8 d=128 bf16"
     out["config"] = cfg
     if do_p and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(q, k, v, wp, args.cpu_rows)

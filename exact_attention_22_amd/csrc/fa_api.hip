@@ -55,6 +55,30 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
 }
 
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens_q, const int* cu_seqlens_k,
+                         int B, int H, int H_kv, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int d, int causal, float scale,
+                         fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+    if (total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1) return FA_ERR_SHAPE;
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_SHAPE;
+    if (count4(total_q, H, d, 1) < 0 || count4(total_k, H_kv, d, 1) < 0) return FA_ERR_SHAPE;
+    if ((int64_t)B * H > INT32_MAX || B == INT32_MAX) return FA_ERR_SHAPE;
+    // a K/V tile (64 rows of H_kv * d values) must lie within a 32-bit byte range
+    if ((int64_t)H_kv * d * 2 * 64 > INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u) ||
+        ((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k, v, o, lse, B, H, max_seqlen_q, max_seqlen_k, d, causal != 0, dtype == FA_BF16,
+                    scale, 0, true, cu_seqlens_q, cu_seqlens_k, H_kv, total_q, total_k};
+    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+}
+
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
     if (!supported_d(d) || num_splits < 1) return 0;
     const int64_t n = count4(num_splits, B, H, Nq);
@@ -98,7 +122,7 @@ const char* fa_status_str(fa_status status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULL: return "a required pointer is NULL";
-        case FA_ERR_SHAPE: return "invalid size: B, H, Nq, Nk must be >= 1, 1 <= num_splits <= Nk, no overflow";
+        case FA_ERR_SHAPE: return "invalid size: B, H, Nq, Nk must be >= 1, 1 <= num_splits <= Nk, H_kv divides H, no overflow";
         case FA_ERR_UNSUPPORTED: return "unsupported: d must be 64 or 128, dtype f16/bf16, finite scale, 16-byte aligned tensors";
         case FA_ERR_WORKSPACE: return "workspace too small";
         case FA_ERR_HIP: return "HIP runtime error at launch";

@@ -68,6 +68,13 @@ struct FwdArgs {
     u32 qsign;         // 0x80008000 flips Q's sign when scale < 0
     int n_qtiles;
     int split_chunk;   // keys per split (split mode)
+    // packed variable-length sequences (varlen mode): q, o [total_q, H, d];
+    // k, v [total_k, H_kv, d]; lse [H, total_q]; sequence b spans offsets
+    // [cu[b], cu[b+1]) of cu_q / cu_k
+    const int* cu_q;
+    const int* cu_k;
+    int H_kv, group;   // group = H / H_kv query heads per K/V head
+    int total_q, total_k, max_q, max_k;
 };
 
 // Key index (within a 32-key block) that accumulator row i stands for: bits 2 and 3 swapped.
@@ -75,8 +82,9 @@ __device__ __forceinline__ int perm_row(int i) {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-template <bool BF16, int D, bool CAUSAL, bool SPLIT>
+template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+    static_assert(!(SPLIT && VARLEN), "split-KV partials take the [B,H,N,d] layout");
     constexpr int ROWB = D * 2;                  // bytes per K/V row
     constexpr int TILE = BC * ROWB;              // bytes per K (or V) tile
     constexpr int NS = D / 16;                   // 16-wide d slices of Q
@@ -87,43 +95,89 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
     // ---- work item -------------------------------------------------------
+    // Workgroup b runs on XCD b % 8 (the hardware dispatches round-robin).
     const int total = gridDim.x;
-    int L = blockIdx.x;
-    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);   // XCD-contiguous ranges
-    const int qt = a.n_qtiles - 1 - (L % a.n_qtiles);             // heaviest first
-    const int rest = L / a.n_qtiles;
-    const int bh = rest % a.BH;
-    const int split = SPLIT ? rest / a.BH : 0;
+    int qt, bh, split = 0;
+    if (VARLEN && ((a.B * a.H_kv) & 7) == 0) {
+        // Packed sequences differ in length, so contiguous ranges would leave one
+        // XCD with the longest sequence: instead K/V group (b, hk) goes to XCD
+        // (b*H_kv + hk) % 8, where its H/H_kv query heads share the L2.
+        const int per_group = a.group * a.n_qtiles;
+        const int j = blockIdx.x >> 3, gi = j / per_group, r = j - gi * per_group;
+        const int grp = gi * 8 + (blockIdx.x & 7);
+        const int b = grp / a.H_kv, hk = grp - b * a.H_kv;
+        qt = a.n_qtiles - 1 - r / a.group;                        // heaviest first
+        bh = b * a.H + hk * a.group + r % a.group;
+    } else {
+        int L = blockIdx.x;
+        if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);   // XCD-contiguous ranges
+        qt = a.n_qtiles - 1 - (L % a.n_qtiles);                   // heaviest first
+        const int rest = L / a.n_qtiles;
+        bh = rest % a.BH;
+        if (SPLIT) split = rest / a.BH;
+    }
+    const int q0 = qt * BR;
+
+    // ---- this item's sequence: sizes, base pointers, row strides -------------
+    int Nq = a.Nq, Nk = a.Nk;
+    const uint16_t* qg;                           // row 0 of this (sequence, head)
+    const uint16_t* kg;
+    const uint16_t* vg;
+    int q_rs = D, kv_rs = D;                      // elements between consecutive rows
+    size_t o0 = (size_t)bh * a.Nq * D;            // element offset of this item's output row 0
+    int o_rs = D;
+    float* lse_g = a.lse + (size_t)bh * a.Nq;
+    if constexpr (VARLEN) {
+        // Offsets come from the caller's device arrays: a sequence whose offsets
+        // leave [0, total], decrease or exceed the declared maximum is skipped,
+        // so no access ever leaves the tensors.
+        const int b = bh / a.H, hq = bh - b * a.H;
+        const int qs = a.cu_q[b], qe = a.cu_q[b + 1], ks0 = a.cu_k[b], ke0 = a.cu_k[b + 1];
+        if (qs < 0 || qe < qs || qe > a.total_q || qe - qs > a.max_q) return;
+        if (ks0 < 0 || ke0 < ks0 || ke0 > a.total_k || ke0 - ks0 > a.max_k) return;
+        Nq = qe - qs;
+        Nk = ke0 - ks0;
+        if (q0 >= Nq) return;
+        const int hk = hq / a.group;
+        q_rs = a.H * D;
+        kv_rs = a.H_kv * D;
+        o_rs = a.H * D;
+        qg = a.q + (size_t)qs * q_rs + (size_t)hq * D;
+        kg = a.k + (size_t)ks0 * kv_rs + (size_t)hk * D;
+        vg = a.v + (size_t)ks0 * kv_rs + (size_t)hk * D;
+        o0 = (size_t)qs * o_rs + (size_t)hq * D;
+        lse_g = a.lse + (size_t)hq * a.total_q + qs;
+    } else {
+        qg = a.q + (size_t)bh * a.Nq * D;
+        kg = a.k + (size_t)bh * a.Nk * D;
+        vg = a.v + (size_t)bh * a.Nk * D;
+    }
+    const int kv_rowb = kv_rs * 2;                // bytes between consecutive K/V rows
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int l32 = lane & 31;
     const int h = lane >> 5;
-    const int q0 = qt * BR;
     const int qw = q0 + 32 * w;
     const int qi = qw + l32;
-    const int off = a.Nk - a.Nq;                  // causal: key j visible iff j <= i + off
+    const int off = Nk - Nq;                      // causal: key j visible iff j <= i + off
 
-    const uint16_t* qg = a.q + (size_t)bh * a.Nq * D;
-    const uint16_t* kg = a.k + (size_t)bh * a.Nk * D;
-    const uint16_t* vg = a.v + (size_t)bh * a.Nk * D;
-
-    int ks = 0, ke = a.Nk;
+    int ks = 0, ke = Nk;
     if (SPLIT) {
-        ks = min(a.Nk, split * a.split_chunk);
-        ke = min(a.Nk, ks + a.split_chunk);
+        ks = min(Nk, split * a.split_chunk);
+        ke = min(Nk, ks + a.split_chunk);
     }
     int hi = ke;
-    if (CAUSAL) hi = min(hi, min(a.Nq, q0 + BR) - 1 + off + 1);
+    if (CAUSAL) hi = min(hi, min(Nq, q0 + BR) - 1 + off + 1);
     const int n_tiles = hi > ks ? (hi - ks + BC - 1) / BC : 0;
 
     // ---- Q fragments, resident for the whole key loop ----------------------
     u32x4 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        if (qi < a.Nq) {
-            qf[s] = *(const u32x4*)(qg + (size_t)qi * D + 16 * s + 8 * h);
+        if (qi < Nq) {
+            qf[s] = *(const u32x4*)(qg + (size_t)qi * q_rs + 16 * s + 8 * h);
             qf[s] ^= a.qsign;
         } else {
             qf[s] = u32x4{0, 0, 0, 0};
@@ -133,21 +187,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // ---- K/V tiles: buffer loads straight into LDS ---------------------------
     // One wave instruction fills 1 KiB of LDS, lane i landing at byte 16*i.  Lane
     // i therefore fetches the global chunk that the swizzled layout stores at
-    // that position; these offsets do not change from tile to tile.  Reads past
-    // the head's last key return zeros (the descriptor's record count).
+    // that position (global rows are kv_rowb bytes apart); these offsets do not
+    // change from tile to tile.  Reads past the sequence's last key return zeros
+    // (the descriptor's record count ends with that key's row).
     constexpr int NPW = TILE / 1024 / 4;         // 1 KiB loads per wave per tensor per tile
     u32 voff[NPW];
 #pragma unroll
     for (int u = 0; u < NPW; ++u) {
         const int pos = (w * NPW + u) * 1024 + lane * 16;
         const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
-        voff[u] = (u32)(row * ROWB + ((pchunk ^ swz<D>(row)) << 4));
+        voff[u] = (u32)(row * kv_rowb + ((pchunk ^ swz<D>(row)) << 4));
     }
     // which = 0 loads the K tile of `tile` into the stage, 1 its V tile
     auto load_half = [&](int tile, unsigned char* stage, int which) {
         const int k0 = ks + tile * BC;
-        const u32 nrec = (u32)(a.Nk - k0) * ROWB;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * D, nrec);
+        const u32 nrec = (u32)(min(Nk - k0, BC) - 1) * kv_rowb + ROWB;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * kv_rs, nrec);
         unsigned char* dst = stage + which * TILE + w * NPW * 1024;
 #pragma unroll
         for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
@@ -266,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         if (clean) break;
         ++n_masked;
     }
-    const int qmax_w = min(qw + 31, a.Nq - 1);
+    const int qmax_w = min(qw + 31, Nq - 1);
     if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -279,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         unsigned char* nxt = (it & 1) ? stage0 : stage1;
         if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
         const int k0 = ks + tile * BC;
-        const bool active = qw < a.Nq && (!CAUSAL || k0 <= qmax_w + off);
+        const bool active = qw < Nq && (!CAUSAL || k0 <= qmax_w + off);
         if (active) tile_step(cur, cur + TILE, k0, std::true_type{}, [] {});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -310,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const float lt = sum_halves(lsum);
     const float inv = (lt == 0.f || lt != lt) ? 1.f : 1.f / lt;
     const float lse_v = (lt == 0.f) ? -INFINITY : (Mu + log2f(lt)) * kLn2;
-    if (qi < a.Nq) {
+    if (qi < Nq) {
         if constexpr (SPLIT) {
             float* op = (float*)a.o + (((size_t)split * a.BH + bh) * a.Nq + qi) * D;
 #pragma unroll
@@ -323,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 }
             if (h == 0) a.lse[((size_t)split * a.BH + bh) * a.Nq + qi] = lse_v;
         } else {
-            uint16_t* op = (uint16_t*)a.o + ((size_t)bh * a.Nq + qi) * D;
+            uint16_t* op = (uint16_t*)a.o + o0 + (size_t)qi * o_rs;
 #pragma unroll
             for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -332,22 +387,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                                       pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
                     *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
                 }
-            if (h == 0) a.lse[(size_t)bh * a.Nq + qi] = lse_v;
+            if (h == 0) lse_g[qi] = lse_v;
         }
     }
 }
 
-template <bool BF16, int D, bool CAUSAL, bool SPLIT>
+template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, SPLIT>), dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, SPLIT, VARLEN>), dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
+// mode: 0 plain [B,H,N,d], 1 split-KV partials, 2 packed variable-length
 template <bool BF16, int D>
-hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, bool split, hipStream_t s) {
-    if (causal)
-        return split ? launch_t<BF16, D, true, true>(a, blocks, s) : launch_t<BF16, D, true, false>(a, blocks, s);
-    return split ? launch_t<BF16, D, false, true>(a, blocks, s) : launch_t<BF16, D, false, false>(a, blocks, s);
+hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, int mode, hipStream_t s) {
+    if (causal) {
+        if (mode == 1) return launch_t<BF16, D, true, true, false>(a, blocks, s);
+        if (mode == 2) return launch_t<BF16, D, true, false, true>(a, blocks, s);
+        return launch_t<BF16, D, true, false, false>(a, blocks, s);
+    }
+    if (mode == 1) return launch_t<BF16, D, false, true, false>(a, blocks, s);
+    if (mode == 2) return launch_t<BF16, D, false, false, true>(a, blocks, s);
+    return launch_t<BF16, D, false, false, false>(a, blocks, s);
 }
 
 }  // namespace
@@ -366,17 +427,26 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     a.BH = p.B * p.H;
     a.c = fabsf(p.scale) * kLog2e;
     a.qsign = p.scale < 0.f ? 0x80008000u : 0u;
-    a.n_qtiles = (p.Nq + BR - 1) / BR;
+    a.n_qtiles = (p.Nq + BR - 1) / BR;        // varlen: Nq is the longest query sequence
     const bool split = p.num_splits > 0;
     const int S = split ? p.num_splits : 1;
     a.split_chunk = split_chunk(p.Nk, S);
+    a.cu_q = p.cu_q;
+    a.cu_k = p.cu_k;
+    a.H_kv = p.varlen ? p.H_kv : p.H;
+    a.group = p.H / a.H_kv;
+    a.total_q = p.total_q;
+    a.total_k = p.total_k;
+    a.max_q = p.Nq;
+    a.max_k = p.Nk;
+    const int mode = p.varlen ? 2 : (split ? 1 : 0);
     const int64_t blocks = (int64_t)a.n_qtiles * a.BH * S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.d == 128)
-        return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, split, stream)
-                      : dispatch_cs<false, 128>(a, (int)blocks, p.causal, split, stream);
-    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, split, stream)
-                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, split, stream);
+        return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, mode, stream)
+                      : dispatch_cs<false, 128>(a, (int)blocks, p.causal, mode, stream);
+    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, mode, stream)
+                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, mode, stream);
 }
 
 }  // namespace fa

@@ -19,6 +19,13 @@ struct FwdParams {
     bool bf16;
     float scale;
     int num_splits;   // 0: plain forward; >= 1: split-KV partials
+    // packed variable-length sequences with grouped K/V heads (then Nq and Nk
+    // are the longest query and key sequences)
+    bool varlen;
+    const int* cu_q;  // device, B + 1 offsets
+    const int* cu_k;
+    int H_kv;
+    int total_q, total_k;
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);

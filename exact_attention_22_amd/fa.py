@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
-SYMBOLS = ("fa_fwd", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_str")
+SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_splitkv_combine",
+           "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -37,6 +38,8 @@ def lib():
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.fa_fwd.restype = i
         L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        L.fa_fwd_varlen.restype = i
+        L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
         L.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
         L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_fwd_splitkv.restype = i
@@ -104,6 +107,40 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     lp = _dev_tensor(lse, "lse", torch.float32)
     _check(lib().fa_fwd(qp, kp, vp, op, lp, B, H, Nq, Nk, d, int(bool(causal)), _scale(scale, d),
                         _DTYPES[q.dtype], _stream(stream)))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
+               scale=None, out=None, lse=None, stream=None):
+    """Packed variable-length sequences with grouped K/V heads.
+
+    q [total_q, H, d], k and v [total_k, H_kv, d] (H_kv divides H), cu_seqlens_q
+    and cu_seqlens_k int32 [B + 1] device tensors of cumulative offsets.  Returns
+    O [total_q, H, d] and LSE [H, total_q] (fp32).  scale defaults to 1/sqrt(d).
+    """
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [total_q, H, d] and k, v [total_k, H_kv, d]")
+    total_q, H, d = q.shape
+    total_k, H_kv = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (total_k, H_kv, d) or tuple(v.shape) != (total_k, H_kv, d):
+        raise ValueError("k and v must be [total_k, H_kv, d] with q's d")
+    if cu_seqlens_q.dim() != 1 or tuple(cu_seqlens_k.shape) != tuple(cu_seqlens_q.shape):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    B = cu_seqlens_q.shape[0] - 1
+    qp, kp, vp = (_dev_tensor(t, n, q.dtype) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    cqp = _dev_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    ckp = _dev_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (H, total_q):
+        raise ValueError("out must be [total_q, H, d] and lse [H, total_q]")
+    op = _dev_tensor(out, "out", q.dtype)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    _check(lib().fa_fwd_varlen(qp, kp, vp, op, lp, cqp, ckp, B, H, H_kv, total_q, total_k,
+                               int(max_seqlen_q), int(max_seqlen_k), d, int(bool(causal)),
+                               _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
     return out, lse
 
 

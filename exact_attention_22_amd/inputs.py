@@ -10,6 +10,9 @@ Workloads (Q, K, V iid N(0, 1), layout [B, H, N, d], scale = 1/sqrt(d)):
   causal_d128     B=4  H=16 Nq=Nk=2048  d=128 fp16  causal
   long_causal     B=1  H=32 Nq=Nk=8192  d=128 bf16  causal, values scaled by 0.5
   decode          B=8  H=32 Nq=1 Nk=32768 d=128 fp16 non-causal, 16 KV splits
+  varlen_gqa      16 packed sequences, lengths log-uniform in [64, 8192] (seeded),
+                  H=32 query heads sharing H_kv=8 K/V heads, d=128 bf16 causal,
+                  Nq = Nk per sequence; layout [total, heads, d]
 These follow the shapes the pages benchmark (randn fp16, d in {64, 128},
 N from 1K to 16K) -- no dataset is involved.
 """
@@ -35,6 +38,8 @@ class Workload:
     mult: float = 1.0        # the long-context workload draws N(0,1) * 0.5
     splits: int = 0          # > 0: decode through split-KV + combine
     seed: int = 42
+    H_kv: int = 0            # > 0: packed variable-length layout with grouped K/V heads
+    seqlens: tuple = ()      # packed layout: per-sequence lengths (queries = keys)
 
     @property
     def scale(self) -> float:
@@ -44,12 +49,23 @@ class Workload:
         return replace(self, **kw)
 
 
+def log_uniform_lengths(n, lo, hi, seed):
+    """n sequence lengths drawn log-uniformly from [lo, hi] by a seeded generator."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.rand(n, generator=g, dtype=torch.float64).tolist()
+    return tuple(int(round(math.exp(math.log(lo) + x * (math.log(hi) - math.log(lo))))) for x in u)
+
+
+_VARLEN_LENS = log_uniform_lengths(16, 64, 8192, 47)
+
 WORKLOADS = [
     Workload("tiny", 1, 1, 128, 128, 64, F16, False, seed=42),
     Workload("prefill_d64", 16, 16, 1024, 1024, 64, F16, False, seed=43),
     Workload("causal_d128", 4, 16, 2048, 2048, 128, F16, True, seed=44),
     Workload("long_causal", 1, 32, 8192, 8192, 128, BF16, True, mult=0.5, seed=45),
     Workload("decode", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=46),
+    Workload("varlen_gqa", len(_VARLEN_LENS), 32, max(_VARLEN_LENS), max(_VARLEN_LENS), 128, BF16, True,
+             seed=47, H_kv=8, seqlens=_VARLEN_LENS),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -70,6 +86,31 @@ def make_qkv(w: Workload, device="cpu"):
         out.append(x.to(w.dtype))
         del x
     return tuple(out)
+
+
+def cu_seqlens(lengths):
+    """Cumulative offsets [0, l0, l0 + l1, ...] of packed sequences (int32)."""
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def make_varlen(w: Workload, device="cpu"):
+    """Packed Q [total, H, d] and K, V [total, H_kv, d] drawn as in make_qkv, plus
+    the cumulative offsets of w.seqlens (the same for queries and keys)."""
+    total = sum(w.seqlens)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    out = []
+    for heads in (w.H, w.H_kv, w.H_kv):
+        x = torch.randn((total, heads, w.d), generator=g, dtype=torch.float32, device=device)
+        if w.mult != 1.0:
+            x.mul_(w.mult)
+        out.append(x.to(w.dtype))
+        del x
+    cu = cu_seqlens(w.seqlens).to(device)
+    return (*out, cu, cu.clone())
 
 
 def make_partials(S, B, H, Nq, d, seed=7, device="cpu", empty_every=0):

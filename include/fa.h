@@ -54,7 +54,8 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL */
-    FA_ERR_SHAPE = 2,       /* B, H, Nq, Nk < 1, num_splits out of [1, Nk], or a size overflows */
+    FA_ERR_SHAPE = 2,       /* B, H, Nq, Nk < 1, num_splits out of [1, Nk], H_kv not dividing H,
+                               or a size overflows */
     FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite scale, misaligned pointer */
     FA_ERR_WORKSPACE = 4,   /* reserved: a workspace too small for the request */
     FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
@@ -68,6 +69,39 @@ typedef enum {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int Nq, int Nk, int d, int causal, float scale,
                  fa_dtype dtype, void* stream);
+
+/*
+ * Prefill over variable-length sequences packed without padding, with K/V heads
+ * shared by groups of query heads (GQA; MQA when H_kv = 1).  Packing skips the
+ * work a padded batch would spend on padding (Ringi, Lecture 25, section 7:
+ * the varlen interface takes the cumulative sequence offsets cu_seqlens);
+ * grouped heads index K/V by h / (H / H_kv) (KingOfEgg, Flash Attention (4),
+ * section 5: K/V index mapped by group, entry point with cu_seqlens).
+ *
+ *   q, o           [total_q, H, d]     dtype (token-major: token t of sequence b
+ *                                       is row cu_seqlens_q[b] + t)
+ *   k, v           [total_k, H_kv, d]  dtype
+ *   lse            [H, total_q]        float32
+ *   cu_seqlens_q   int32 device array of B + 1 offsets: 0 = cu[0] <= cu[1] <= ...
+ *   cu_seqlens_k   <= cu[B] = total_q (resp. total_k); sequence b's queries are
+ *                  tokens [cu_q[b], cu_q[b+1]) and its keys [cu_k[b], cu_k[b+1])
+ *   max_seqlen_q/k bounds on every sequence's query / key count
+ *
+ * Query head h of sequence b attends to K/V head h / (H / H_kv) of the same
+ * sequence; causal visibility is bottom-right aligned within each sequence (key
+ * j visible to query i iff j <= i + Nk_b - Nq_b), and a query that sees no key
+ * (also when Nk_b = 0) gets O = 0 and LSE = -inf.  Requirements: B, H, H_kv >= 1,
+ * H % H_kv == 0, 1 <= max_seqlen_q <= total_q, 1 <= max_seqlen_k <= total_k;
+ * cu_seqlens 4-byte aligned.  The offsets live on the device and are not read by
+ * the host: a sequence whose offsets fall outside [0, total], decrease, or span
+ * more than max_seqlen is skipped by the kernel (its rows of o and lse are left
+ * unwritten) and no memory outside the tensors is accessed.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k,
+                        int B, int H, int H_kv, int total_q, int total_k,
+                        int max_seqlen_q, int max_seqlen_k, int d, int causal, float scale,
+                        fa_dtype dtype, void* stream);
 
 /*
  * Bytes of partial results fa_fwd_splitkv writes for the given shape:

@@ -63,6 +63,30 @@ def test_fwd_validation():
     assert fwd(o=MIS) == fa.FA_ERR_UNSUPPORTED
 
 
+def varlen(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, B=2, H=4, H_kv=2, total_q=16, total_k=24, max_q=9,
+           max_k=13, d=128, causal=1, scale=0.1, dtype=1):
+    return fa.lib().fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, H_kv, total_q, total_k, max_q, max_k,
+                                  d, causal, scale, dtype, NULL)
+
+
+def test_varlen_validation():
+    assert varlen(cq=NULL) == fa.FA_ERR_NULL
+    assert varlen(ck=NULL) == fa.FA_ERR_NULL
+    assert varlen(v=NULL) == fa.FA_ERR_NULL
+    assert varlen(H=4, H_kv=3) == fa.FA_ERR_SHAPE      # H_kv must divide H
+    assert varlen(H_kv=0) == fa.FA_ERR_SHAPE
+    assert varlen(B=0) == fa.FA_ERR_SHAPE
+    assert varlen(total_q=0) == fa.FA_ERR_SHAPE
+    assert varlen(max_q=17) == fa.FA_ERR_SHAPE          # longer than the whole batch
+    assert varlen(max_k=0) == fa.FA_ERR_SHAPE
+    assert varlen(H=1 << 20, H_kv=1 << 20) == fa.FA_ERR_SHAPE
+    assert varlen(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert varlen(dtype=5) == fa.FA_ERR_UNSUPPORTED
+    assert varlen(scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
+    assert varlen(k=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert varlen(cq=ctypes.c_void_p(0x10002)) == fa.FA_ERR_UNSUPPORTED
+
+
 def split(q=A, k=A, v=A, op=A, lp=A, B=1, H=1, Nq=1, Nk=8, d=128, causal=0, scale=0.1, S=2, dtype=1):
     return fa.lib().fa_fwd_splitkv(q, k, v, op, lp, B, H, Nq, Nk, d, causal, scale, S, dtype, NULL)
 
