@@ -108,6 +108,23 @@ class Oracle:
             return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
         return o, lse
 
+    # -- grouped K/V heads in the [B, H, N, d] layout ----------------------
+    @staticmethod
+    def expand_kv_heads(t, H):
+        """[B, H_kv, N, d] -> [B, H, N, d]: K/V head g serves the H // H_kv
+        consecutive query heads g*G .. g*G + G-1 (KingOfEgg, "Flash Attention (4)",
+        section 5: K/V indexed by head group)."""
+        H_kv = t.shape[1]
+        if H % H_kv != 0:
+            raise ValueError("H_kv must divide H")
+        return t.repeat_interleave(H // H_kv, dim=1).contiguous()
+
+    def attention_gqa(self, q, k, v, causal, scale, rows=None, key_range=None, nthreads=None):
+        """attention() with k, v [B, H_kv, Nk, d]: query head h reads K/V head h // (H // H_kv)."""
+        H = q.shape[1]
+        return self.attention(q, self.expand_kv_heads(k, H), self.expand_kv_heads(v, H), causal, scale,
+                              rows=rows, key_range=key_range, nthreads=nthreads)
+
     # -- packed variable-length sequences, grouped K/V heads -------------
     def attention_varlen(self, q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, rows=None,
                          nthreads=None):
@@ -157,10 +174,12 @@ class Oracle:
         return [(min(Nk, s * chunk), min(Nk, (s + 1) * chunk)) for s in range(num_splits)]
 
     def split_partials(self, q, k, v, causal, scale, num_splits, rows=None, nthreads=None):
-        """Per-split normalised (O_s, LSE_s): attention restricted to each key chunk."""
+        """Per-split normalised (O_s, LSE_s): attention restricted to each key chunk
+        (k, v may carry fewer heads than q: grouped K/V heads)."""
         outs, lses = [], []
+        attn = self.attention_gqa if k.shape[1] != q.shape[1] else self.attention
         for kr in self.split_ranges(k.shape[2], num_splits):
-            o, l = self.attention(q, k, v, causal, scale, rows=rows, key_range=kr, nthreads=nthreads)
+            o, l = attn(q, k, v, causal, scale, rows=rows, key_range=kr, nthreads=nthreads)
             outs.append(o)
             lses.append(l)
         return np.stack(outs), np.stack(lses)

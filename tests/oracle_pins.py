@@ -379,7 +379,28 @@ def pin_varlen_rows(orc):
     _close(rl, lse.T.reshape(-1)[rows], 0.0, "varlen selected rows LSE")
 
 
+def pin_dense_grouped_heads(orc):
+    """Grouped K/V heads in the [B, H, N, d] layout equal the packed-sequence oracle
+    (whose head grouping is pinned above) on the same data with uniform lengths."""
+    for H, H_kv in ((8, 2), (4, 1), (6, 3)):
+        for causal in (False, True):
+            B, Nq, Nk, d, dt = 2, 9, 13, 16, torch.float16
+            q = _rand((B, H, Nq, d), dt, 1400 + H)
+            k = _rand((B, H_kv, Nk, d), dt, 1500 + H)
+            v = _rand((B, H_kv, Nk, d), dt, 1600 + H)
+            o, lse = orc.attention_gqa(q, k, v, causal, 0.35, nthreads=2)
+
+            def pack(t):
+                return t.permute(0, 2, 1, 3).reshape(-1, t.shape[1], d).contiguous()
+            cq = np.arange(B + 1, dtype=np.int32) * Nq
+            ck = np.arange(B + 1, dtype=np.int32) * Nk
+            ro, rl = orc.attention_varlen(pack(q), pack(k), pack(v), cq, ck, causal, 0.35, nthreads=2)
+            _close(o, ro.reshape(B, Nq, H, d).transpose(0, 2, 1, 3), 0.0, f"dense GQA O H={H} H_kv={H_kv}")
+            _close(lse, rl.reshape(H, B, Nq).transpose(1, 0, 2), 0.0, f"dense GQA LSE H={H} H_kv={H_kv}")
+
+
 ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
-            pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows]
+            pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows,
+            pin_dense_grouped_heads]

@@ -63,3 +63,15 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         except (AssertionError, RuntimeError, FloatingPointError) as e:
             caught.append(f"{pin.__name__}: {str(e)[:80]}")
     assert caught, f"no pin catches the mutant {name}"
+
+
+def test_dense_grouped_heads_mapping_mutant_is_caught():
+    """Tiling K/V heads (h -> h % H_kv) instead of repeating them per group fails
+    the dense grouped-heads pin."""
+    class Tiled(oracle.Oracle):
+        @staticmethod
+        def expand_kv_heads(t, H):
+            return t.repeat(1, H // t.shape[1], 1, 1).contiguous()
+
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_dense_grouped_heads(Tiled())
