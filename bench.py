@@ -4,7 +4,8 @@ One step = one pass of the whole path over resident synthetic inputs:
   * prefill: fa_fwd on the long-context causal workload
     (B=1, H=32, Nq=Nk=8192, d=128, bf16, N(0,1)*0.5), and
   * decode: fa_fwd_splitkv + fa_splitkv_combine on the decode workload
-    (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits), and
+    (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits), the same with the 32
+    query heads sharing 8 K/V heads (decode_gqa), and
   * varlen: fa_fwd_varlen on 16 packed causal sequences (lengths log-uniform in
     [64, 8192], 20752 tokens) with 32 query heads sharing 8 K/V heads, d=128, bf16.
 `value` is the prefill throughput in TFLOP/s with FLOPs = 4*B*H*Nq*Nk*d, halved
@@ -103,7 +104,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=40000)
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -119,9 +120,10 @@ def main():
     dev = torch.device("cuda:0")
     fa.lib()
 
-    wp, wd, wv = BY_NAME["long_causal"], BY_NAME["decode"], BY_NAME["varlen_gqa"]
+    wp, wd, wv, wg = BY_NAME["long_causal"], BY_NAME["decode"], BY_NAME["varlen_gqa"], BY_NAME["decode_gqa"]
     do_p, do_d = args.only in ("all", "prefill"), args.only in ("all", "decode")
     do_v = args.only in ("all", "varlen")
+    do_g = args.only in ("all", "decode_gqa")
     if do_p:
         q, k, v = make_qkv(wp, device=dev)
         o = torch.empty_like(q)
@@ -133,6 +135,12 @@ def main():
         lp = torch.empty((S, wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
         do_ = torch.empty_like(dq)
         dlse = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+    if do_g:
+        gq, gk, gv = make_qkv(wg, device=dev)
+        gop = torch.empty((wg.splits, wg.B, wg.H, wg.Nq, wg.d), dtype=torch.float32, device=dev)
+        glp = torch.empty((wg.splits, wg.B, wg.H, wg.Nq), dtype=torch.float32, device=dev)
+        go = torch.empty_like(gq)
+        glse = torch.empty((wg.B, wg.H, wg.Nq), dtype=torch.float32, device=dev)
     if do_v:
         vq, vk, vv, vcq, vck = make_varlen(wv, device=dev)
         vo = torch.empty_like(vq)
@@ -150,7 +158,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e = [ev() for _ in range(5)]
+        e = [ev() for _ in range(7)]
         e[0].record(stream)
         if do_p:
             fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse, stream=stream)
@@ -166,6 +174,13 @@ def main():
             fa.fwd_varlen(vq, vk, vv, vcq, vck, vmax, vmax, causal=wv.causal, scale=wv.scale, out=vo,
                           lse=vlse, stream=stream)
         e[4].record(stream)
+        if do_g:
+            fa.fwd_splitkv_gqa(gq, gk, gv, wg.splits, causal=wg.causal, scale=wg.scale, o_part=gop, lse_part=glp,
+                               stream=stream)
+        e[5].record(stream)
+        if do_g:
+            fa.splitkv_combine(gop, glp, wg.dtype, out=go, lse=glse, stream=stream)
+        e[6].record(stream)
         if rec is not None:
             rec.append(e)
 
@@ -183,6 +198,7 @@ def main():
         return sum(r[i].elapsed_time(r[j]) for r in recs) / len(recs)
 
     t_fwd, t_split, t_comb, t_var = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
+    t_gsplit, t_gcomb = avg_ms(4, 5), avg_ms(5, 6)
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic"}
@@ -220,6 +236,24 @@ def main():
             cfg["workload"] = "decode: B=8 H=32 Nq=1 Nk=32768 d=128 fp16 16 splits"
         cfg["decode"] = {"B": wd.B, "H": wd.H, "Nq": wd.Nq, "Nk": wd.Nk, "d": wd.d, "dtype": "fp16",
                          "splits": S}
+    if do_g:
+        # bytes the method must move: Q, O (B*H*d each), K, V (B*H_kv*Nk*d each), LSE
+        gb = 2 * (2 * wg.B * wg.H * wg.d + 2 * wg.B * wg.H_kv * wg.Nk * wg.d) + 4 * wg.B * wg.H
+        tg = t_gsplit + t_gcomb
+        out["decode_gqa"] = {"GB_per_s": gb / (tg * 1e-3) / 1e9, "hbm_frac": gb / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "us_total": tg * 1e3, "us_splitkv": t_gsplit * 1e3, "us_combine": t_gcomb * 1e3,
+                             "algorithmic_bytes": gb}
+        gsplit_bytes = gb - 2 * wg.B * wg.H * wg.d - 4 * wg.B * wg.H
+        out["roofline_decode_gqa"] = {"bound": "hbm", "achieved": gsplit_bytes / (t_gsplit * 1e-3) / 1e9,
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gsplit_bytes / (t_gsplit * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                      "traffic": read_traffic("decode_gqa", source_hash(DEC_SOURCES)),
+                                      "kernel": "decode_kernel<fp16, d=128, 4 query heads per workgroup>"}
+        cfg["decode_gqa"] = {"B": wg.B, "H": wg.H, "H_kv": wg.H_kv, "Nq": wg.Nq, "Nk": wg.Nk, "d": wg.d,
+                             "dtype": "fp16", "splits": wg.splits}
+        if not (do_p or do_d or do_v):
+            out.update({"value": out["decode_gqa"]["GB_per_s"], "unit": "GB/s", "dtype": "f16"})
+            cfg["workload"] = "decode_gqa: B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 fp16 16 splits"
     if do_v:
         fl = sum(attn_flops(1, wv.H, n, n, wv.d, wv.causal) for n in wv.seqlens)
         tf = fl / (t_var * 1e-3) / 1e12

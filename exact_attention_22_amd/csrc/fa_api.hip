@@ -39,6 +39,43 @@ fa_status check_common(int B, int H, int Nq, int Nk, int d, float scale, fa_dtyp
 
 fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+fa_status check_heads(int H, int H_kv) {
+    return (H_kv < 1 || H % H_kv != 0) ? FA_ERR_SHAPE : FA_OK;
+}
+
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                   int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if ((st = check_heads(H, H_kv)) != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, dtype == FA_BF16, scale, 0};
+    p.H_kv = H_kv;
+    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+}
+
+fa_status splitkv_impl(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
+                       int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, int num_splits,
+                       fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
+    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if ((st = check_heads(H, H_kv)) != FA_OK) return st;
+    if (num_splits < 1 || num_splits > Nk) return FA_ERR_SHAPE;
+    if (count4(num_splits, B, H, (int64_t)Nq * d) < 0) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) || ((uintptr_t)lse_part & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k, v, o_part, lse_part, B, H, Nq, Nk, d, causal != 0, dtype == FA_BF16, scale,
+                    num_splits};
+    p.H_kv = H_kv;
+    // One query row sees every key whatever the causal flag (j <= 0 + Nk - 1):
+    // the streaming kernel serves it; longer query blocks use the tiled kernel.
+    if (Nq == 1) return from_hip(fa::launch_decode(p, (hipStream_t)stream));
+    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -46,13 +83,13 @@ extern "C" {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int Nq, int Nk, int d, int causal, float scale,
                  fa_dtype dtype, void* stream) {
-    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
-    if (st != FA_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
-        return FA_ERR_UNSUPPORTED;
-    fa::FwdParams p{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, dtype == FA_BF16, scale, 0};
-    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+    return fwd_impl(q, k, v, o, lse, B, H, H, Nq, Nk, d, causal, scale, dtype, stream);
+}
+
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale,
+                     fa_dtype dtype, void* stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, causal, scale, dtype, stream);
 }
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -89,19 +126,14 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                          int B, int H, int Nq, int Nk, int d, int causal, float scale,
                          int num_splits, fa_dtype dtype, void* stream) {
-    if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
-    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
-    if (st != FA_OK) return st;
-    if (num_splits < 1 || num_splits > Nk) return FA_ERR_SHAPE;
-    if (count4(num_splits, B, H, (int64_t)Nq * d) < 0) return FA_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) || ((uintptr_t)lse_part & 3u))
-        return FA_ERR_UNSUPPORTED;
-    fa::FwdParams p{q, k, v, o_part, lse_part, B, H, Nq, Nk, d, causal != 0, dtype == FA_BF16, scale,
-                    num_splits};
-    // One query row sees every key whatever the causal flag (j <= 0 + Nk - 1):
-    // the streaming kernel serves it; longer query blocks use the tiled kernel.
-    if (Nq == 1) return from_hip(fa::launch_decode(p, (hipStream_t)stream));
-    return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
+    return splitkv_impl(q, k, v, o_part, lse_part, B, H, H, Nq, Nk, d, causal, scale, num_splits, dtype, stream);
+}
+
+fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                             int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale,
+                             int num_splits, fa_dtype dtype, void* stream) {
+    return splitkv_impl(q, k, v, o_part, lse_part, B, H, H_kv, Nq, Nk, d, causal, scale, num_splits, dtype,
+                        stream);
 }
 
 fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,

@@ -16,6 +16,11 @@
 // to cover HBM latency.  At the end the 16 (d = 128) or 32 (d = 64) partial
 // states of the workgroup merge through LDS with the online-softmax identity
 // (Ringi, Lecture 25, section 2.2).
+//
+// Grouped K/V heads (KingOfEgg, "Flash Attention (4)", section 5): the GP query
+// heads of one workgroup read the same K/V head, so the workgroup streams that
+// head's chunk once and scores every loaded key row against all GP queries;
+// decode bytes per query head fall by GP.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -31,6 +36,7 @@ struct DecArgs {
     int BH, Nk, S;
     int split_chunk;
     float c;   // scale * log2(e), sign included
+    int H, H_kv, group;   // query heads, K/V heads, query heads per K/V head
 };
 
 template <int CTRL>
@@ -61,17 +67,19 @@ __device__ __forceinline__ void widen8(u32x4 x, float* f) {
     }
 }
 
-template <bool BF16, int D>
+// GP: query heads per workgroup (a divisor of the group size).
+template <bool BF16, int D, int GP>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     constexpr int CH = D / 8;          // lanes per key row
     constexpr int KPI = 64 / CH;       // key rows per wavefront load
-    constexpr int U = 8;               // key groups in flight per step
-    constexpr int NP = 4 * KPI;        // partial states per workgroup
-    __shared__ float s_m[NP], s_l[NP];
-    __shared__ __attribute__((aligned(16))) float s_o[NP * D];
+    constexpr int U = GP >= 4 ? 4 : 8; // key groups in flight per step
+    constexpr int NP = 4 * KPI;        // partial states per workgroup and query head
+    __shared__ float s_m[GP][NP], s_l[GP][NP];
+    __shared__ __attribute__((aligned(16))) float s_o[GP][NP * D];
 
     const int split = blockIdx.x % a.S;
-    const int bh = blockIdx.x / a.S;
+    const int bh0 = (blockIdx.x / a.S) * GP;          // first of GP consecutive query heads
+    const int bkv = (bh0 / a.H) * a.H_kv + (bh0 % a.H) / a.group;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = lane % CH, r = lane / CH;
 
@@ -79,17 +87,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     const int ke = min(a.Nk, ks + a.split_chunk);
     const int ngroups = (ke - ks + KPI - 1) / KPI;
 
-    const uint16_t* kg = a.k + (size_t)bh * a.Nk * D;
-    const uint16_t* vg = a.v + (size_t)bh * a.Nk * D;
+    const uint16_t* kg = a.k + (size_t)bkv * a.Nk * D;
+    const uint16_t* vg = a.v + (size_t)bkv * a.Nk * D;
 
-    float qv[8];
-    widen8<BF16>(*(const u32x4*)(a.q + (size_t)bh * D + 8 * c), qv);
+    float qv[GP][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] *= a.c;
+    for (int g = 0; g < GP; ++g) {
+        widen8<BF16>(*(const u32x4*)(a.q + (size_t)(bh0 + g) * D + 8 * c), qv[g]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[g][i] *= a.c;
+    }
 
-    float M = -INFINITY, l = 0.f, acc[8];
+    float M[GP], l[GP], acc[GP][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int g = 0; g < GP; ++g) {
+        M[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+    }
 
     for (int g0 = w; g0 < ngroups; g0 += 4 * U) {
         u32x4 kr[U], vr[U];
@@ -105,58 +121,72 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
                 vr[u] = u32x4{0, 0, 0, 0};
             }
         }
-        float s[U];
-        float mx = -INFINITY;
+        float s[GP][U];
+        float mx[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float kf[8];
             widen8<BF16>(kr[u], kf);
-            float part = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qv[i], kf[i], part);
-            s[u] = row_sum<CH>(part);
-            if (key[u] >= ke) s[u] = -INFINITY;
-            mx = fmaxf(mx, s[u]);
+            for (int g = 0; g < GP; ++g) {
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qv[g][i], kf[i], part);
+                s[g][u] = row_sum<CH>(part);
+                if (key[u] >= ke) s[g][u] = -INFINITY;
+                mx[g] = fmaxf(mx[g], s[g][u]);
+            }
         }
-        const float Mn = fmaxf(M, mx);
-        const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M - Mn);
-        M = Mn;
-        const float Mg = (M == -INFINITY) ? 0.f : M;
-        l *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+        for (int g = 0; g < GP; ++g) {
+            const float Mn = fmaxf(M[g], mx[g]);
+            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M[g] - Mn);
+            M[g] = Mn;
+            l[g] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float p = exp2_fast(s[u] - Mg);
-            l += p;
             float vf[8];
             widen8<BF16>(vr[u], vf);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(p, vf[i], acc[i]);
+            for (int g = 0; g < GP; ++g) {
+                const float p = exp2_fast(s[g][u] - ((M[g] == -INFINITY) ? 0.f : M[g]));
+                l[g] += p;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(p, vf[i], acc[g][i]);
+            }
         }
     }
 
-    // merge the workgroup's partial states
+    // merge the workgroup's partial states, per query head
     const int pidx = w * KPI + r;
-    if (c == 0) {
-        s_m[pidx] = M;
-        s_l[pidx] = l;
-    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_o[pidx * D + 8 * c + i] = acc[i];
+    for (int g = 0; g < GP; ++g) {
+        if (c == 0) {
+            s_m[g][pidx] = M[g];
+            s_l[g][pidx] = l[g];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_o[g][pidx * D + 8 * c + i] = acc[g][i];
+    }
     __syncthreads();
-    if (tid < D) {
+    for (int t = tid; t < GP * D; t += 256) {
+        const int g = t / D, col = t % D;
         float Ms = -INFINITY;
-        for (int i = 0; i < NP; ++i) Ms = fmaxf(Ms, s_m[i]);
+        for (int i = 0; i < NP; ++i) Ms = fmaxf(Ms, s_m[g][i]);
         float den = 0.f, num = 0.f;
         for (int i = 0; i < NP; ++i) {
-            const float wgt = (s_m[i] == -INFINITY) ? 0.f : exp2_fast(s_m[i] - Ms);
-            den = __builtin_fmaf(wgt, s_l[i], den);
-            num = __builtin_fmaf(wgt, s_o[i * D + tid], num);
+            const float wgt = (s_m[g][i] == -INFINITY) ? 0.f : exp2_fast(s_m[g][i] - Ms);
+            den = __builtin_fmaf(wgt, s_l[g][i], den);
+            num = __builtin_fmaf(wgt, s_o[g][i * D + col], num);
         }
-        const size_t row = (size_t)split * a.BH + bh;
-        a.o_part[row * D + tid] = den > 0.f ? num / den : 0.f;
-        if (tid == 0) a.lse_part[row] = den > 0.f ? (Ms + log2f(den)) * kLn2 : -INFINITY;
+        const size_t row = (size_t)split * a.BH + bh0 + g;
+        a.o_part[row * D + col] = den > 0.f ? num / den : 0.f;
+        if (col == 0) a.lse_part[row] = den > 0.f ? (Ms + log2f(den)) * kLn2 : -INFINITY;
     }
 }
 
@@ -195,6 +225,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (lane == 0) lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
+template <bool BF16, int D>
+hipError_t launch_dec(const DecArgs& a, int gp, int blocks, hipStream_t stream) {
+    switch (gp) {
+        case 8: hipLaunchKernelGGL((decode_kernel<BF16, D, 8>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2>), dim3(blocks), dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<BF16, D, 1>), dim3(blocks), dim3(256), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
@@ -209,16 +250,16 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
     a.S = p.num_splits;
     a.split_chunk = split_chunk(p.Nk, p.num_splits);
     a.c = p.scale * kLog2e;
-    const int64_t blocks = (int64_t)a.BH * a.S;
+    a.H = p.H;
+    a.H_kv = p.H_kv > 0 ? p.H_kv : p.H;
+    a.group = p.H / a.H_kv;
+    // query heads per workgroup: the largest of 8, 4, 2, 1 dividing the group
+    const int gp = a.group % 8 == 0 ? 8 : a.group % 4 == 0 ? 4 : a.group % 2 == 0 ? 2 : 1;
+    const int64_t blocks = (int64_t)a.BH / gp * a.S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (p.d == 128) {
-        if (p.bf16) hipLaunchKernelGGL((decode_kernel<true, 128>), dim3((int)blocks), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<false, 128>), dim3((int)blocks), dim3(256), 0, stream, a);
-    } else {
-        if (p.bf16) hipLaunchKernelGGL((decode_kernel<true, 64>), dim3((int)blocks), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<false, 64>), dim3((int)blocks), dim3(256), 0, stream, a);
-    }
-    return hipGetLastError();
+    if (p.d == 128) return p.bf16 ? launch_dec<true, 128>(a, gp, (int)blocks, stream)
+                                  : launch_dec<false, 128>(a, gp, (int)blocks, stream);
+    return p.bf16 ? launch_dec<true, 64>(a, gp, (int)blocks, stream) : launch_dec<false, 64>(a, gp, (int)blocks, stream);
 }
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,

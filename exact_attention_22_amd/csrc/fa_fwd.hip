@@ -148,9 +148,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         o0 = (size_t)qs * o_rs + (size_t)hq * D;
         lse_g = a.lse + (size_t)hq * a.total_q + qs;
     } else {
+        // [B, H, N, d] queries; keys and values [B, H_kv, N, d], query head h
+        // reading K/V head h / group (group = 1 without grouped heads)
+        const int bkv = a.group == 1 ? bh : (bh / a.H) * a.H_kv + (bh % a.H) / a.group;
         qg = a.q + (size_t)bh * a.Nq * D;
-        kg = a.k + (size_t)bh * a.Nk * D;
-        vg = a.v + (size_t)bh * a.Nk * D;
+        kg = a.k + (size_t)bkv * a.Nk * D;
+        vg = a.v + (size_t)bkv * a.Nk * D;
     }
     const int kv_rowb = kv_rs * 2;                // bytes between consecutive K/V rows
 
@@ -433,7 +436,7 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     a.split_chunk = split_chunk(p.Nk, S);
     a.cu_q = p.cu_q;
     a.cu_k = p.cu_k;
-    a.H_kv = p.varlen ? p.H_kv : p.H;
+    a.H_kv = p.H_kv > 0 ? p.H_kv : p.H;
     a.group = p.H / a.H_kv;
     a.total_q = p.total_q;
     a.total_k = p.total_k;

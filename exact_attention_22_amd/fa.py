@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
-SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_splitkv_combine",
-           "fa_status_str")
+SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
+           "fa_fwd_splitkv_gqa", "fa_splitkv_combine", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -38,6 +38,10 @@ def lib():
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.fa_fwd.restype = i
         L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        L.fa_fwd_gqa.restype = i
+        L.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+        L.fa_fwd_splitkv_gqa.restype = i
+        L.fa_fwd_splitkv_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
         L.fa_fwd_varlen.restype = i
         L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
         L.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
@@ -79,16 +83,22 @@ def _dev_tensor(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _qkv(q, k, v):
+def _qkv(q, k, v, grouped=False):
+    """Pointers and sizes of [B, H, Nq, d] queries and [B, H_kv, Nk, d] keys/values
+    (H_kv = H unless grouped)."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
-        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    Nk, H_kv = k.shape[2], k.shape[1]
+    if not grouped and H_kv != H:
+        raise ValueError("k and v must have q's H heads (fwd_gqa / fwd_splitkv_gqa take fewer)")
+    if tuple(k.shape) != (B, H_kv, Nk, d) or tuple(v.shape) != (B, H_kv, Nk, d):
+        raise ValueError("k and v must be [B, H_kv, Nk, d] with q's B and d")
     ptrs = [_dev_tensor(t, n, q.dtype) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    if grouped:
+        return ptrs, (B, H, H_kv, Nq, Nk, d)
     return ptrs, (B, H, Nq, Nk, d)
 
 
@@ -107,6 +117,20 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     lp = _dev_tensor(lse, "lse", torch.float32)
     _check(lib().fa_fwd(qp, kp, vp, op, lp, B, H, Nq, Nk, d, int(bool(causal)), _scale(scale, d),
                         _DTYPES[q.dtype], _stream(stream)))
+    return out, lse
+
+
+def fwd_gqa(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """fwd with K/V heads shared by groups of query heads: k, v [B, H_kv, Nk, d]."""
+    (qp, kp, vp), (B, H, H_kv, Nq, Nk, d) = _qkv(q, k, v, grouped=True)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("out must be [B, H, Nq, d] and lse [B, H, Nq]")
+    op = _dev_tensor(out, "out", q.dtype)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    _check(lib().fa_fwd_gqa(qp, kp, vp, op, lp, B, H, H_kv, Nq, Nk, d, int(bool(causal)), _scale(scale, d),
+                            _DTYPES[q.dtype], _stream(stream)))
     return out, lse
 
 
@@ -165,6 +189,23 @@ def fwd_splitkv(q, k, v, num_splits, causal=False, scale=None, o_part=None, lse_
     return o_part, lse_part
 
 
+def fwd_splitkv_gqa(q, k, v, num_splits, causal=False, scale=None, o_part=None, lse_part=None, stream=None):
+    """fwd_splitkv with grouped K/V heads: k, v [B, H_kv, Nk, d]."""
+    (qp, kp, vp), (B, H, H_kv, Nq, Nk, d) = _qkv(q, k, v, grouped=True)
+    S = int(num_splits)
+    if o_part is None:
+        o_part = torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device)
+    if tuple(o_part.shape) != (S, B, H, Nq, d) or tuple(lse_part.shape) != (S, B, H, Nq):
+        raise ValueError("o_part must be [S, B, H, Nq, d] and lse_part [S, B, H, Nq]")
+    opp = _dev_tensor(o_part, "o_part", torch.float32)
+    lpp = _dev_tensor(lse_part, "lse_part", torch.float32)
+    _check(lib().fa_fwd_splitkv_gqa(qp, kp, vp, opp, lpp, B, H, H_kv, Nq, Nk, d, int(bool(causal)),
+                                    _scale(scale, d), S, _DTYPES[q.dtype], _stream(stream)))
+    return o_part, lse_part
+
+
 def splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, stream=None):
     """Merge split partials into O (dtype) and LSE (fp32)."""
     if dtype not in _DTYPES:
@@ -185,6 +226,8 @@ def splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, stream=None):
 
 
 def decode(q, k, v, num_splits=16, causal=False, scale=None, stream=None, o_part=None, lse_part=None):
-    """Split-KV forward followed by the combine, both on the same stream."""
-    o_part, lse_part = fwd_splitkv(q, k, v, num_splits, causal, scale, o_part, lse_part, stream)
+    """Split-KV forward followed by the combine, both on the same stream; k and v
+    may carry fewer heads than q (grouped K/V heads)."""
+    split = fwd_splitkv_gqa if k.dim() == 4 and q.dim() == 4 and k.shape[1] != q.shape[1] else fwd_splitkv
+    o_part, lse_part = split(q, k, v, num_splits, causal, scale, o_part, lse_part, stream)
     return splitkv_combine(o_part, lse_part, q.dtype, stream=stream)

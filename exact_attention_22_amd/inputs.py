@@ -10,6 +10,8 @@ Workloads (Q, K, V iid N(0, 1), layout [B, H, N, d], scale = 1/sqrt(d)):
   causal_d128     B=4  H=16 Nq=Nk=2048  d=128 fp16  causal
   long_causal     B=1  H=32 Nq=Nk=8192  d=128 bf16  causal, values scaled by 0.5
   decode          B=8  H=32 Nq=1 Nk=32768 d=128 fp16 non-causal, 16 KV splits
+  decode_gqa      as decode with the 32 query heads sharing H_kv=8 K/V heads
+                  (K, V [B, 8, Nk, d])
   varlen_gqa      16 packed sequences, lengths log-uniform in [64, 8192] (seeded),
                   H=32 query heads sharing H_kv=8 K/V heads, d=128 bf16 causal,
                   Nq = Nk per sequence; layout [total, heads, d]
@@ -38,8 +40,8 @@ class Workload:
     mult: float = 1.0        # the long-context workload draws N(0,1) * 0.5
     splits: int = 0          # > 0: decode through split-KV + combine
     seed: int = 42
-    H_kv: int = 0            # > 0: packed variable-length layout with grouped K/V heads
-    seqlens: tuple = ()      # packed layout: per-sequence lengths (queries = keys)
+    H_kv: int = 0            # K/V heads when grouped (0: H)
+    seqlens: tuple = ()      # non-empty: packed layout with these lengths (queries = keys)
 
     @property
     def scale(self) -> float:
@@ -64,6 +66,7 @@ WORKLOADS = [
     Workload("causal_d128", 4, 16, 2048, 2048, 128, F16, True, seed=44),
     Workload("long_causal", 1, 32, 8192, 8192, 128, BF16, True, mult=0.5, seed=45),
     Workload("decode", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=46),
+    Workload("decode_gqa", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=48, H_kv=8),
     Workload("varlen_gqa", len(_VARLEN_LENS), 32, max(_VARLEN_LENS), max(_VARLEN_LENS), 128, BF16, True,
              seed=47, H_kv=8, seqlens=_VARLEN_LENS),
 ]
@@ -71,7 +74,8 @@ BY_NAME = {w.name: w for w in WORKLOADS}
 
 
 def make_qkv(w: Workload, device="cpu"):
-    """Draw Q, then K, then V as float32 N(0,1) (times w.mult), cast to w.dtype.
+    """Draw Q [B,H,Nq,d], then K and V [B,H_kv,Nk,d] as float32 N(0,1) (times
+    w.mult), cast to w.dtype.
 
     The generator runs on `device`, so the bits depend on it; callers that need
     the same data on the CPU copy the tensors rather than drawing again.
@@ -79,8 +83,9 @@ def make_qkv(w: Workload, device="cpu"):
     g = torch.Generator(device=device)
     g.manual_seed(w.seed)
     out = []
-    for n in (w.Nq, w.Nk, w.Nk):
-        x = torch.randn((w.B, w.H, n, w.d), generator=g, dtype=torch.float32, device=device)
+    hk = w.H_kv or w.H
+    for n, heads in ((w.Nq, w.H), (w.Nk, hk), (w.Nk, hk)):
+        x = torch.randn((w.B, heads, n, w.d), generator=g, dtype=torch.float32, device=device)
         if w.mult != 1.0:
             x.mul_(w.mult)
         out.append(x.to(w.dtype))

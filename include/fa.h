@@ -71,6 +71,16 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  fa_dtype dtype, void* stream);
 
 /*
+ * fa_fwd with K/V heads shared by groups of query heads (GQA; MQA when
+ * H_kv = 1): k and v are [B, H_kv, Nk, d] and query head h attends to K/V head
+ * h / (H / H_kv) (KingOfEgg, Flash Attention (4), section 5: K/V index mapped by
+ * group).  H % H_kv must be 0, else FA_ERR_SHAPE.  With H_kv = H this is fa_fwd.
+ */
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale,
+                     fa_dtype dtype, void* stream);
+
+/*
  * Prefill over variable-length sequences packed without padding, with K/V heads
  * shared by groups of query heads (GQA; MQA when H_kv = 1).  Packing skips the
  * work a padded batch would spend on padding (Ringi, Lecture 25, section 7:
@@ -124,6 +134,17 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v,
                          float* o_part, float* lse_part,
                          int B, int H, int Nq, int Nk, int d, int causal, float scale,
                          int num_splits, fa_dtype dtype, void* stream);
+
+/*
+ * fa_fwd_splitkv with grouped K/V heads: k and v are [B, H_kv, Nk, d], query head
+ * h reads K/V head h / (H / H_kv); partials and their combine are as above (one
+ * row per query head).  For Nq = 1 a workgroup serves up to 8 query heads of one
+ * group and streams their shared K/V chunk once.  H % H_kv must be 0.
+ */
+fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v,
+                             float* o_part, float* lse_part,
+                             int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale,
+                             int num_splits, fa_dtype dtype, void* stream);
 
 /*
  * Split-KV forward, second half: merge the partials with the online-softmax

@@ -63,6 +63,29 @@ def test_fwd_validation():
     assert fwd(o=MIS) == fa.FA_ERR_UNSUPPORTED
 
 
+def gqa(q=A, k=A, v=A, o=A, lse=A, B=1, H=8, H_kv=2, Nq=8, Nk=8, d=128, causal=1, scale=0.1, dtype=1):
+    return fa.lib().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, causal, scale, dtype, NULL)
+
+
+def split_gqa(q=A, k=A, v=A, op=A, lp=A, B=1, H=8, H_kv=2, Nq=1, Nk=64, d=128, causal=0, scale=0.1, S=4, dtype=0):
+    return fa.lib().fa_fwd_splitkv_gqa(q, k, v, op, lp, B, H, H_kv, Nq, Nk, d, causal, scale, S, dtype, NULL)
+
+
+def test_gqa_validation():
+    assert gqa(k=NULL) == fa.FA_ERR_NULL
+    assert gqa(H_kv=3) == fa.FA_ERR_SHAPE
+    assert gqa(H_kv=0) == fa.FA_ERR_SHAPE
+    assert gqa(H=4, H_kv=8) == fa.FA_ERR_SHAPE        # more K/V heads than query heads
+    assert gqa(Nq=0) == fa.FA_ERR_SHAPE
+    assert gqa(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert gqa(v=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert split_gqa(lp=NULL) == fa.FA_ERR_NULL
+    assert split_gqa(H_kv=5) == fa.FA_ERR_SHAPE
+    assert split_gqa(S=65) == fa.FA_ERR_SHAPE
+    assert split_gqa(dtype=9) == fa.FA_ERR_UNSUPPORTED
+    assert split_gqa(q=MIS) == fa.FA_ERR_UNSUPPORTED
+
+
 def varlen(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, B=2, H=4, H_kv=2, total_q=16, total_k=24, max_q=9,
            max_k=13, d=128, causal=1, scale=0.1, dtype=1):
     return fa.lib().fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, H_kv, total_q, total_k, max_q, max_k,

@@ -1,0 +1,107 @@
+"""GPU parity of the grouped K/V head entry points (fa_fwd_gqa, and the split-KV
+decode fa_fwd_splitkv_gqa + fa_splitkv_combine) through the C ABI against the
+fp64 oracle.
+
+Small shapes are compared on every output element, for group sizes that run the
+decode kernel with 1, 2, 4 and 8 query heads per workgroup (and a group of 16
+split over two workgroups); the decode_gqa workload is compared at full size on
+sampled rows, through the same calls the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_22_amd import fa
+from exact_attention_22_amd.inputs import BY_NAME, make_qkv
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+F16, BF16 = torch.float16, torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def rnd(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype)
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+FWD = [  # B, H, H_kv, Nq, Nk, d, causal, dtype
+    (2, 8, 2, 200, 200, 128, True, BF16),
+    (1, 4, 1, 129, 300, 64, False, F16),      # MQA
+    (1, 6, 3, 333, 100, 128, True, F16),      # Nq > Nk
+    (2, 4, 4, 64, 65, 64, True, BF16),        # no grouping
+]
+
+
+@pytest.mark.parametrize("case", FWD, ids=lambda c: f"B{c[0]}H{c[1]}kv{c[2]}q{c[3]}k{c[4]}d{c[5]}c{int(c[6])}")
+def test_fwd_gqa(dev, oracle_lib, case):
+    B, H, H_kv, Nq, Nk, d, causal, dt = case
+    q, k, v = rnd((B, H, Nq, d), dt, 1), rnd((B, H_kv, Nk, d), dt, 2), rnd((B, H_kv, Nk, d), dt, 3)
+    say(f"fa_fwd_gqa {case}")
+    o, lse = fa.fwd_gqa(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle_lib.attention_gqa(q, k, v, causal, 1 / math.sqrt(d))
+    parity.check(o, lse, ro, rl, dt, f"fwd_gqa {case}")
+
+
+DEC = [  # B, H, H_kv, Nk, d, splits, dtype
+    (2, 8, 8, 1000, 128, 4, F16),      # 1 query head per workgroup
+    (2, 8, 4, 777, 128, 3, BF16),      # 2
+    (1, 8, 2, 3000, 128, 8, F16),      # 4
+    (1, 16, 2, 2049, 64, 5, BF16),     # 8
+    (1, 32, 2, 513, 128, 2, F16),      # group of 16: two workgroups of 8
+    (2, 6, 2, 100, 64, 7, F16),        # group of 3: one query head per workgroup
+    (1, 8, 1, 4096, 128, 16, BF16),    # MQA
+]
+
+
+@pytest.mark.parametrize("case", DEC, ids=lambda c: f"B{c[0]}H{c[1]}kv{c[2]}k{c[3]}d{c[4]}S{c[5]}")
+def test_decode_gqa(dev, oracle_lib, case):
+    B, H, H_kv, Nk, d, S, dt = case
+    q, k, v = rnd((B, H, 1, d), dt, 4), rnd((B, H_kv, Nk, d), dt, 5), rnd((B, H_kv, Nk, d), dt, 6)
+    say(f"fa_fwd_splitkv_gqa + combine {case}")
+    op, lp = fa.fwd_splitkv_gqa(q.to(dev), k.to(dev), v.to(dev), S)
+    o, lse = fa.splitkv_combine(op, lp, dt)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    rop, rlp = oracle_lib.split_partials(q, k, v, False, scale, S)
+    parity.check(op, lp, rop, rlp, dt, f"partials {case}")
+    ro, rl = oracle_lib.attention_gqa(q, k, v, False, scale)
+    parity.check(o, lse, ro, rl, dt, f"decode_gqa {case}")
+
+
+def test_splitkv_gqa_multi_row(dev, oracle_lib):
+    """Nq > 1 takes the tiled kernel's split mode with grouped heads."""
+    B, H, H_kv, Nq, Nk, d, S = 1, 8, 2, 70, 900, 128, 3
+    q, k, v = rnd((B, H, Nq, d), F16, 7), rnd((B, H_kv, Nk, d), F16, 8), rnd((B, H_kv, Nk, d), F16, 9)
+    for causal in (False, True):
+        say(f"fa_fwd_splitkv_gqa Nq={Nq} causal={causal}")
+        o, lse = fa.decode(q.to(dev), k.to(dev), v.to(dev), num_splits=S, causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = oracle_lib.attention_gqa(q, k, v, causal, 1 / math.sqrt(d))
+        parity.check(o, lse, ro, rl, F16, f"splitkv_gqa multi-row causal={causal}")
+
+
+def test_decode_gqa_workload(dev, oracle_lib):
+    """Full-size decode_gqa (the benchmark's calls), sampled rows vs the oracle."""
+    w = BY_NAME["decode_gqa"]
+    q, k, v = make_qkv(w)
+    say(f"decode_gqa B={w.B} H={w.H} H_kv={w.H_kv} Nk={w.Nk} S={w.splits}")
+    o, lse = fa.decode(q.to(dev), k.to(dev), v.to(dev), num_splits=w.splits, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = parity.sample_rows(w.B, w.H, w.Nq, n_random=96, seed=3)
+    ro, rl = oracle_lib.attention_gqa(q, k, v, w.causal, w.scale, rows=rows)
+    idx = torch.from_numpy(rows).to(dev)
+    parity.check(o.reshape(-1, w.d)[idx], lse.reshape(-1)[idx], ro, rl, w.dtype, "decode_gqa sampled")
