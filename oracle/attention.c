@@ -311,3 +311,187 @@ int oracle_combine(const double *o_part, const double *lse_part, int S, int64_t 
     }
     return 0;
 }
+
+/*
+ * Backward pass (gradients of a loss with upstream gradient dO = dL/dO), from
+ * the chain rule as Ringi, "Lecture 25", section 3.3 states it for P =
+ * softmax(S):
+ *   dV = P^T dO;   dP = dO V^T;   dS = P o (dP - rowsum(dP o P));
+ *   dQ = dS K;     dK = dS^T Q
+ * with the scores here S = sigma * Q K^T, so the chain rule adds sigma to dQ and
+ * dK (dS is the gradient with respect to the scaled scores).  Masked keys have
+ * P = 0 and so contribute nothing; a row that sees no key has P = 0 throughout.
+ * The statistics of every query row of the (b, h) heads that are needed are
+ * computed first (m, l and D_i = rowsum(dP o P)); then
+ *   dq_i = sigma * sum_j dS_ij k_j                 for the requested query rows,
+ *   dv_j = sum_i P_ij dO_i,  dk_j = sigma * sum_i dS_ij q_i   for the requested key rows.
+ * Layouts [B, H, N, d]; q_rows are flat (b*H + h)*Nq + i, k_rows (b*H + h)*Nk + j;
+ * NULL means all.  Outputs: dq [n_q, d], dk and dv [n_k, d].
+ */
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    int dtype, H, Nq, Nk, d, causal;
+    double sigma;
+    double *m, *l, *D;          /* per query row of the needed heads */
+    int64_t *head_slot;         /* (b*H + h) -> slot in m/l/D, or -1 */
+    const int64_t *q_rows, *k_rows;
+    int64_t n_q, n_k;
+    double *dq, *dk, *dv;
+    int64_t first, last;        /* worker's slice: phase 0 rows of needed heads, 1 q rows, 2 k rows */
+    int phase;
+    const int64_t *stat_rows;   /* phase 0: flat query rows needing statistics */
+} bjob_t;
+
+static int row_visible_end(int i, int Nq, int Nk, int causal) {
+    int hi = Nk;
+    if (causal) hi = causal_end(i, Nq, Nk, 0, hi);
+    return hi;
+}
+
+/* dO_i . v_j and sigma * q_i . k_j in double */
+static double dot_rows(const uint16_t *a, const uint16_t *b, int d, int dtype) {
+    double acc = 0.0;
+    for (int t = 0; t < d; ++t) acc += decode(a[t], dtype) * decode(b[t], dtype);
+    return acc;
+}
+
+static void bwd_stats(const bjob_t *jb, int64_t flat) {
+    const int d = jb->d, Nq = jb->Nq, Nk = jb->Nk;
+    const int64_t bh = flat / Nq;
+    const int i = (int)(flat % Nq);
+    const int64_t slot = jb->head_slot[bh] * Nq + i;
+    const uint16_t *qi = jb->q + ((size_t)bh * Nq + i) * d;
+    const uint16_t *gi = jb->dout + ((size_t)bh * Nq + i) * d;
+    const uint16_t *kp = jb->k + (size_t)bh * Nk * d;
+    const uint16_t *vp = jb->v + (size_t)bh * Nk * d;
+    const int hi = row_visible_end(i, Nq, Nk, jb->causal);
+    double m = -INFINITY;
+    for (int j = 0; j < hi; ++j) {
+        double s = jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype);
+        if (s > m) m = s;
+    }
+    double l = 0.0;
+    for (int j = 0; j < hi; ++j) l += exp(jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype) - m);
+    double D = 0.0;                                           /* rowsum(dP o P) */
+    for (int j = 0; j < hi; ++j) {
+        double p = exp(jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype) - m) / l;
+        D += p * dot_rows(gi, vp + (size_t)j * d, d, jb->dtype);
+    }
+    jb->m[slot] = m;
+    jb->l[slot] = l;
+    jb->D[slot] = hi > 0 ? D : 0.0;
+}
+
+static void bwd_q_row(const bjob_t *jb, int64_t flat, double *dq) {
+    const int d = jb->d, Nq = jb->Nq, Nk = jb->Nk;
+    const int64_t bh = flat / Nq;
+    const int i = (int)(flat % Nq);
+    const int64_t slot = jb->head_slot[bh] * Nq + i;
+    const uint16_t *qi = jb->q + ((size_t)bh * Nq + i) * d;
+    const uint16_t *gi = jb->dout + ((size_t)bh * Nq + i) * d;
+    const uint16_t *kp = jb->k + (size_t)bh * Nk * d;
+    const uint16_t *vp = jb->v + (size_t)bh * Nk * d;
+    const int hi = row_visible_end(i, Nq, Nk, jb->causal);
+    for (int t = 0; t < d; ++t) dq[t] = 0.0;
+    for (int j = 0; j < hi; ++j) {
+        const uint16_t *kj = kp + (size_t)j * d;
+        double p = exp(jb->sigma * dot_rows(qi, kj, d, jb->dtype) - jb->m[slot]) / jb->l[slot];
+        double ds = p * (dot_rows(gi, vp + (size_t)j * d, d, jb->dtype) - jb->D[slot]);
+        for (int t = 0; t < d; ++t) dq[t] += jb->sigma * ds * decode(kj[t], jb->dtype);
+    }
+}
+
+static void bwd_k_row(const bjob_t *jb, int64_t flat, double *dk, double *dv) {
+    const int d = jb->d, Nq = jb->Nq, Nk = jb->Nk;
+    const int64_t bh = flat / Nk;
+    const int j = (int)(flat % Nk);
+    const uint16_t *kj = jb->k + ((size_t)bh * Nk + j) * d;
+    const uint16_t *vj = jb->v + ((size_t)bh * Nk + j) * d;
+    for (int t = 0; t < d; ++t) dk[t] = dv[t] = 0.0;
+    for (int i = 0; i < Nq; ++i) {
+        if (j >= row_visible_end(i, Nq, Nk, jb->causal)) continue;   /* key j masked for query i */
+        const int64_t slot = jb->head_slot[bh] * Nq + i;
+        const uint16_t *qi = jb->q + ((size_t)bh * Nq + i) * d;
+        const uint16_t *gi = jb->dout + ((size_t)bh * Nq + i) * d;
+        double p = exp(jb->sigma * dot_rows(qi, kj, d, jb->dtype) - jb->m[slot]) / jb->l[slot];
+        double ds = p * (dot_rows(gi, vj, d, jb->dtype) - jb->D[slot]);
+        for (int t = 0; t < d; ++t) {
+            dv[t] += p * decode(gi[t], jb->dtype);
+            dk[t] += jb->sigma * ds * decode(qi[t], jb->dtype);
+        }
+    }
+}
+
+static void *bwd_worker(void *arg) {
+    bjob_t *jb = (bjob_t *)arg;
+    for (int64_t r = jb->first; r < jb->last; ++r) {
+        if (jb->phase == 0) bwd_stats(jb, jb->stat_rows[r]);
+        else if (jb->phase == 1) bwd_q_row(jb, jb->q_rows ? jb->q_rows[r] : r, jb->dq + r * jb->d);
+        else bwd_k_row(jb, jb->k_rows ? jb->k_rows[r] : r, jb->dk + r * jb->d, jb->dv + r * jb->d);
+    }
+    return NULL;
+}
+
+static void bwd_run(const bjob_t *base, int phase, int64_t n, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = n > 0 ? (int)n : 1;
+    bjob_t jobs[256];
+    pthread_t tid[256];
+    int started[256];
+    for (int w = 0; w < nthreads; ++w) {
+        jobs[w] = *base;
+        jobs[w].phase = phase;
+        jobs[w].first = n * w / nthreads;
+        jobs[w].last = n * (w + 1) / nthreads;
+        started[w] = pthread_create(&tid[w], NULL, bwd_worker, &jobs[w]) == 0;
+        if (!started[w]) bwd_worker(&jobs[w]);
+    }
+    for (int w = 0; w < nthreads; ++w)
+        if (started[w]) pthread_join(tid[w], NULL);
+}
+
+int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                         int dtype, int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                         const int64_t *q_rows, int64_t n_q, const int64_t *k_rows, int64_t n_k,
+                         double *dq, double *dk, double *dv, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || n_q < 0 || n_k < 0) return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    const int64_t BH = (int64_t)B * H;
+    if (!q_rows && n_q != BH * Nq) return -1;
+    if (!k_rows && n_k != BH * Nk) return -1;
+    for (int64_t r = 0; q_rows && r < n_q; ++r)
+        if (q_rows[r] < 0 || q_rows[r] >= BH * Nq) return -1;
+    for (int64_t r = 0; k_rows && r < n_k; ++r)
+        if (k_rows[r] < 0 || k_rows[r] >= BH * Nk) return -1;
+    /* heads whose row statistics are needed */
+    int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)BH);
+    if (!slot) return -2;
+    for (int64_t h = 0; h < BH; ++h) slot[h] = -1;
+    int64_t nheads = 0;
+    for (int64_t r = 0; r < n_q; ++r) {
+        int64_t h = (q_rows ? q_rows[r] : r) / Nq;
+        if (slot[h] < 0) slot[h] = nheads++;
+    }
+    for (int64_t r = 0; r < n_k; ++r) {
+        int64_t h = (k_rows ? k_rows[r] : r) / Nk;
+        if (slot[h] < 0) slot[h] = nheads++;
+    }
+    const int64_t nstat = nheads * Nq;
+    double *m = (double *)malloc(sizeof(double) * (size_t)(nstat > 0 ? nstat : 1));
+    double *l = (double *)malloc(sizeof(double) * (size_t)(nstat > 0 ? nstat : 1));
+    double *D = (double *)malloc(sizeof(double) * (size_t)(nstat > 0 ? nstat : 1));
+    int64_t *srows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nstat > 0 ? nstat : 1));
+    if (!m || !l || !D || !srows) { free(slot); free(m); free(l); free(D); free(srows); return -2; }
+    for (int64_t h = 0, n = 0; h < BH; ++h)
+        if (slot[h] >= 0)
+            for (int i = 0; i < Nq; ++i) srows[slot[h] * Nq + i] = h * Nq + i, ++n;
+    bjob_t base = {q, k, v, dout, dtype, H, Nq, Nk, d, causal, (double)scale, m, l, D, slot,
+                   q_rows, k_rows, n_q, n_k, dq, dk, dv, 0, 0, 0, srows};
+    bwd_run(&base, 0, nstat, nthreads);
+    bwd_run(&base, 1, n_q, nthreads);
+    bwd_run(&base, 2, n_k, nthreads);
+    free(slot); free(m); free(l); free(D); free(srows);
+    return 0;
+}

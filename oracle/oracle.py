@@ -57,6 +57,11 @@ class Oracle:
             _u16p, _u16p, _u16p, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p,
             ctypes.c_int, ctypes.c_float, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+        lib.oracle_attention_bwd.restype = ctypes.c_int
+        lib.oracle_attention_bwd.argtypes = [
+            _u16p, _u16p, _u16p, _u16p, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            _i64p, ctypes.c_int64, _i64p, ctypes.c_int64, _f64p, _f64p, _f64p, ctypes.c_int]
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_combine.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                        _f64p, _f64p]
@@ -107,6 +112,43 @@ class Oracle:
         if rows is None:
             return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
         return o, lse
+
+    # -- backward -------------------------------------------------------------
+    def attention_bwd(self, q, k, v, dout, causal, scale, q_rows=None, k_rows=None, nthreads=None):
+        """fp64 gradients dQ, dK, dV of attention for the upstream gradient dout
+        (Ringi, "Lecture 25", section 3.3, with the scale carried through).
+
+        q, dout [B,H,Nq,d]; k, v [B,H,Nk,d].  q_rows (flat (b*H+h)*Nq + i) and
+        k_rows (flat (b*H+h)*Nk + j) select rows; then dq is [len(q_rows), d] and
+        dk, dv [len(k_rows), d], otherwise full [B,H,N,d] arrays.
+        """
+        if not (q.dtype == k.dtype == v.dtype == dout.dtype):
+            raise TypeError("q, k, v, dout must share a dtype")
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
+        if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d) or tuple(dout.shape) != tuple(q.shape):
+            raise ValueError("k, v must be [B,H,Nk,d] and dout [B,H,Nq,d]")
+        bits = [_bits(t) for t in (q, k, v, dout)]
+        qr = None if q_rows is None else np.ascontiguousarray(np.asarray(q_rows, dtype=np.int64))
+        kr = None if k_rows is None else np.ascontiguousarray(np.asarray(k_rows, dtype=np.int64))
+        n_q = B * H * Nq if qr is None else qr.size
+        n_k = B * H * Nk if kr is None else kr.size
+        dq = np.empty((max(n_q, 1), d), dtype=np.float64)
+        dk = np.empty((max(n_k, 1), d), dtype=np.float64)
+        dv = np.empty((max(n_k, 1), d), dtype=np.float64)
+        rc = self.lib.oracle_attention_bwd(
+            *(_ptr(b, _u16p) for b in bits), _DTYPE_CODE[q.dtype], B, H, Nq, Nk, d, int(bool(causal)),
+            float(scale), _ptr(qr, _i64p) if qr is not None else None, n_q,
+            _ptr(kr, _i64p) if kr is not None else None, n_k,
+            _ptr(dq, _f64p), _ptr(dk, _f64p), _ptr(dv, _f64p), nthreads or default_threads())
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
+        dq, dk, dv = dq[:n_q], dk[:n_k], dv[:n_k]
+        if qr is None:
+            dq = dq.reshape(B, H, Nq, d)
+        if kr is None:
+            dk, dv = dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d)
+        return dq, dk, dv
 
     # -- grouped K/V heads in the [B, H, N, d] layout ----------------------
     @staticmethod

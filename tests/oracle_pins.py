@@ -399,8 +399,106 @@ def pin_dense_grouped_heads(orc):
             _close(lse, rl.reshape(H, B, Nq).transpose(1, 0, 2), 0.0, f"dense GQA LSE H={H} H_kv={H_kv}")
 
 
+# -- backward (Ringi, "Lecture 25", section 3.3) ------------------------------
+
+def _torch_grads(q, k, v, dout, causal, scale):
+    """fp64 autograd of softmax(scale Q K^T + mask) V, rows without keys giving 0."""
+    qd, kd, vd = (t.double().requires_grad_(True) for t in (q, k, v))
+    vis = torch.from_numpy(_visible(q.shape[2], k.shape[2], causal))
+    s = float(np.float32(scale)) * (qd @ kd.transpose(-1, -2))
+    s = s.masked_fill(~vis, -math.inf)
+    empty = ~vis.any(dim=1)
+    p = torch.softmax(s.masked_fill(empty[:, None], 0.0), dim=-1).masked_fill(empty[:, None], 0.0)
+    o = p @ vd
+    o.backward(dout.double())
+    return qd.grad.numpy(), kd.grad.numpy(), vd.grad.numpy()
+
+
+BWD_CASES = [  # B, H, Nq, Nk, d, causal, scale
+    (1, 2, 7, 13, 8, False, 0.3), (1, 2, 13, 7, 8, True, 0.3), (2, 1, 16, 16, 16, True, -0.45),
+    (1, 1, 1, 9, 8, False, 1.7), (1, 1, 20, 6, 8, True, 0.5), (1, 2, 12, 12, 64, True, 0.125),
+]
+
+
+def pin_bwd_autograd(orc):
+    """dQ, dK, dV equal torch autograd of the plain forward in fp64."""
+    for ci, (B, H, Nq, Nk, d, causal, scale) in enumerate(BWD_CASES):
+        for dt in DTYPES:
+            q, k, v, g = (_rand((B, H, n, d), dt, 1700 + 10 * ci + s) for s, n in enumerate((Nq, Nk, Nk, Nq)))
+            dq, dk, dv = orc.attention_bwd(q, k, v, g, causal, scale, nthreads=2)
+            rq, rk, rv = _torch_grads(q, k, v, g, causal, scale)
+            _close(dq, rq, 1e-12, f"bwd dQ case {ci} {dt}")
+            _close(dk, rk, 1e-12, f"bwd dK case {ci} {dt}")
+            _close(dv, rv, 1e-12, f"bwd dV case {ci} {dt}")
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of L = sum(O o dO) (O from torch's fp64 attention) match
+    the gradients to within the O(h^2) truncation error."""
+    B, H, Nq, Nk, d = 1, 1, 3, 4, 4
+    for causal in (False, True):
+        q, k, v, g = (_rand((B, H, n, d), torch.float16, 1800 + s, -1, 1, 0.125)
+                      for s, n in enumerate((Nq, Nk, Nk, Nq)))
+        vis = torch.from_numpy(_visible(Nq, Nk, causal))
+        sc = 0.7
+
+        def loss(qd, kd, vd):
+            o = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=vis, scale=float(np.float32(sc)))
+            return float((o * g.double()).sum())
+        dq, dk, dv = orc.attention_bwd(q, k, v, g, causal, sc, nthreads=1)
+        base = [q.double(), k.double(), v.double()]
+        h = 1e-5
+        for which, grad in enumerate((dq, dk, dv)):
+            fd = np.zeros_like(grad)
+            for idx in np.ndindex(*grad.shape):
+                plus = [t.clone() for t in base]
+                minus = [t.clone() for t in base]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+            _close(grad, fd, 1e-8, f"finite differences input {which} causal={causal}")
+
+
+def pin_bwd_scale_zero(orc):
+    """scale = 0: uniform weights, so dQ = dK = 0 and dV_j = sum over rows i that see
+    key j of dO_i / |V_i|."""
+    for causal in (False, True):
+        B, H, Nq, Nk, d = 1, 1, 10, 7, 8
+        q, k, v, g = (_rand((B, H, n, d), torch.bfloat16, 1900 + s) for s, n in enumerate((Nq, Nk, Nk, Nq)))
+        dq, dk, dv = orc.attention_bwd(q, k, v, g, causal, 0.0, nthreads=1)
+        vis = _visible(Nq, Nk, causal).astype(np.float64)
+        cnt = vis.sum(axis=1)
+        w = vis / np.maximum(cnt, 1)[:, None]
+        _close(dq, np.zeros_like(dq), 0.0, "scale 0 dQ")
+        _close(dk, np.zeros_like(dk), 0.0, "scale 0 dK")
+        _close(dv[0, 0], w.T @ g.double().numpy()[0, 0], 1e-14, f"scale 0 dV causal={causal}")
+
+
+def pin_bwd_key_gradient_sums_to_zero(orc):
+    """Every row of dS sums to 0 (P o (dP - rowsum(dP o P))), so sum_j dK_j = 0: the
+    loss does not change when one vector is added to every key."""
+    for causal in (False, True):
+        B, H, Nq, Nk, d = 2, 2, 11, 9, 16
+        q, k, v, g = (_rand((B, H, n, d), torch.float16, 2000 + s) for s, n in enumerate((Nq, Nk, Nk, Nq)))
+        _, dk, _ = orc.attention_bwd(q, k, v, g, causal, 0.4, nthreads=1)
+        _close(dk.sum(axis=2), np.zeros((B, H, d)), 1e-12, f"sum of dK causal={causal}")
+
+
+def pin_bwd_rows(orc):
+    """Selected query and key rows equal the same rows of the full result."""
+    B, H, Nq, Nk, d = 2, 2, 9, 12, 8
+    q, k, v, g = (_rand((B, H, n, d), torch.float16, 2100 + s) for s, n in enumerate((Nq, Nk, Nk, Nq)))
+    dq, dk, dv = orc.attention_bwd(q, k, v, g, True, 0.3, nthreads=1)
+    qr, kr = np.array([0, 5, 20, 35]), np.array([3, 11, 30, 47])
+    sq, sk, sv = orc.attention_bwd(q, k, v, g, True, 0.3, q_rows=qr, k_rows=kr, nthreads=2)
+    _close(sq, dq.reshape(-1, d)[qr], 0.0, "bwd selected dQ rows")
+    _close(sk, dk.reshape(-1, d)[kr], 0.0, "bwd selected dK rows")
+    _close(sv, dv.reshape(-1, d)[kr], 0.0, "bwd selected dV rows")
+
+
 ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
             pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows,
-            pin_dense_grouped_heads]
+            pin_dense_grouped_heads, pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_scale_zero,
+            pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows]

@@ -21,8 +21,9 @@ MUTANTS = [
     ("unnormalised_output", "for (int t = 0; t < d; ++t) o_row[t] /= l;", "for (int t = 0; t < d; ++t) o_row[t] /= 1.0;"),
     ("k_row_stride", "const uint16_t *kj = kp + (size_t)j * kstride;", "const uint16_t *kj = kp + (size_t)j;"),
     ("v_row_of_first_key", "const uint16_t *vj = vp + (size_t)j * kstride;", "const uint16_t *vj = vp + (size_t)lo * kstride;"),
-    ("q_row_of_key", "jb->q + ((size_t)bh * Nq + i) * d;", "jb->q + ((size_t)bh * Nq) * d;"),
-    ("head_stride", "const uint16_t *kp = jb->k + (size_t)bh * Nk * d;", "const uint16_t *kp = jb->k;"),
+    ("q_row_of_key", "*qp = jb->q + ((size_t)bh * Nq + i) * d;", "*qp = jb->q + ((size_t)bh * Nq) * d;"),
+    ("head_stride", "i) * d;\n    const uint16_t *kp = jb->k + (size_t)bh * Nk * d;\n    const uint16_t *vp = jb->v + (size_t)bh * Nk * d;\n\n    int lo",
+     "i) * d;\n    const uint16_t *kp = jb->k;\n    const uint16_t *vp = jb->v + (size_t)bh * Nk * d;\n\n    int lo"),
     ("f16_exponent_bias", "expo - 25", "expo - 24"),
     ("f16_subnormal", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     ("bf16_exponent_bias", "expo - 134", "expo - 133"),
@@ -41,6 +42,13 @@ MUTANTS = [
      "const uint16_t *qp = jb->q + ((size_t)token * H) * d;"),
     ("varlen_sequence_search", "while (b + 1 < jb->B && jb->cu_q[b + 1] <= token) ++b;",
      "while (b + 1 < jb->B && jb->cu_q[b + 1] < token) ++b;"),
+    ("bwd_rowsum_without_p", "D += p * dot_rows(gi, vp", "D += dot_rows(gi, vp"),
+    ("bwd_dq_without_scale", "dq[t] += jb->sigma * ds * decode(kj[t], jb->dtype);", "dq[t] += ds * decode(kj[t], jb->dtype);"),
+    ("bwd_dk_without_scale", "dk[t] += jb->sigma * ds * decode(qi[t], jb->dtype);", "dk[t] += ds * decode(qi[t], jb->dtype);"),
+    ("bwd_dk_from_keys", "dk[t] += jb->sigma * ds * decode(qi[t], jb->dtype);", "dk[t] += jb->sigma * ds * decode(kj[t], jb->dtype);"),
+    ("bwd_dv_from_ds", "dv[t] += p * decode(gi[t], jb->dtype);", "dv[t] += ds * decode(gi[t], jb->dtype);"),
+    ("bwd_causal_off_by_one", "if (j >= row_visible_end(i, Nq, Nk, jb->causal)) continue;", "if (j > row_visible_end(i, Nq, Nk, jb->causal)) continue;"),
+    ("bwd_ds_sign", "double ds = p * (dot_rows(gi, vp + (size_t)j * d, d, jb->dtype) - jb->D[slot]);", "double ds = p * (dot_rows(gi, vp + (size_t)j * d, d, jb->dtype) + jb->D[slot]);"),
     ("empty_row_lse_zero", "if (hi <= lo) { *lse_out = -INFINITY; return; }", "if (hi <= lo) { *lse_out = 0.0; return; }"),
 ]
 
