@@ -6,6 +6,7 @@ One step = one pass of the whole path over resident synthetic inputs:
   * decode: fa_fwd_splitkv + fa_splitkv_combine on the decode workload
     (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits), the same with the 32
     query heads sharing 8 K/V heads (decode_gqa), and
+  * bwd: fa_bwd on the long-context causal workload (dO ~ N(0,1)), and
   * varlen: fa_fwd_varlen on 16 packed causal sequences (lengths log-uniform in
     [64, 8192], 20752 tokens) with 32 query heads sharing 8 K/V heads, d=128, bf16.
 `value` is the prefill throughput in TFLOP/s with FLOPs = 4*B*H*Nq*Nk*d, halved
@@ -104,7 +105,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa", "bwd"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=40000)
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -124,6 +125,7 @@ def main():
     do_p, do_d = args.only in ("all", "prefill"), args.only in ("all", "decode")
     do_v = args.only in ("all", "varlen")
     do_g = args.only in ("all", "decode_gqa")
+    do_b = args.only in ("all", "bwd")
     if do_p:
         q, k, v = make_qkv(wp, device=dev)
         o = torch.empty_like(q)
@@ -135,6 +137,19 @@ def main():
         lp = torch.empty((S, wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
         do_ = torch.empty_like(dq)
         dlse = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+    if do_b:
+        if not do_p:
+            q, k, v = make_qkv(wp, device=dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device=dev)
+        fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wp.seed + 100)
+        bdo = torch.randn(tuple(q.shape), generator=gen, device=dev, dtype=torch.float32).to(wp.dtype)
+        bdq, bdk, bdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(fa.bwd_workspace_bytes(wp.B, wp.H, wp.Nq) // 4, dtype=torch.float32, device=dev)
+        # the backward reads the forward's o and lse: keep them fixed while timing
+        bo, blse = o.clone(), lse.clone()
     if do_g:
         gq, gk, gv = make_qkv(wg, device=dev)
         gop = torch.empty((wg.splits, wg.B, wg.H, wg.Nq, wg.d), dtype=torch.float32, device=dev)
@@ -158,7 +173,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e = [ev() for _ in range(7)]
+        e = [ev() for _ in range(8)]
         e[0].record(stream)
         if do_p:
             fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse, stream=stream)
@@ -181,6 +196,10 @@ def main():
         if do_g:
             fa.splitkv_combine(gop, glp, wg.dtype, out=go, lse=glse, stream=stream)
         e[6].record(stream)
+        if do_b:
+            fa.bwd(q, k, v, bo, blse, bdo, causal=wp.causal, scale=wp.scale, dq=bdq, dk=bdk, dv=bdv, workspace=bws,
+                   stream=stream)
+        e[7].record(stream)
         if rec is not None:
             rec.append(e)
 
@@ -199,6 +218,7 @@ def main():
 
     t_fwd, t_split, t_comb, t_var = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
     t_gsplit, t_gcomb = avg_ms(4, 5), avg_ms(5, 6)
+    t_bwd = avg_ms(6, 7)
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic"}
@@ -236,6 +256,20 @@ def main():
             cfg["workload"] = "decode: B=8 H=32 Nq=1 Nk=32768 d=128 fp16 16 splits"
         cfg["decode"] = {"B": wd.B, "H": wd.H, "Nq": wd.Nq, "Nk": wd.Nk, "d": wd.d, "dtype": "fp16",
                          "splits": S}
+    if do_b:
+        # algorithmic work of the backward: its five products (recompute S, dP, dV, dK,
+        # dQ) = 2.5 x the forward's two
+        fl = 2.5 * attn_flops(wp.B, wp.H, wp.Nq, wp.Nk, wp.d, wp.causal)
+        tb = fl / (t_bwd * 1e-3) / 1e12
+        out["bwd"] = {"TFLOP_per_s": tb, "pct_mfma_peak": 100.0 * tb / PEAK_TFLOPS[wp.dtype], "avg_us": t_bwd * 1e3,
+                      "flop_per_launch": fl}
+        out["roofline_bwd"] = {"bound": "mfma", "achieved": tb, "peak": PEAK_TFLOPS[wp.dtype], "unit": "TFLOP/s",
+                               "frac": tb / PEAK_TFLOPS[wp.dtype], "traffic": None,
+                               "kernel": "bwd_delta + bwd_dkdv + bwd_dq <bf16, d=128, causal>"}
+        cfg["bwd"] = {"B": wp.B, "H": wp.H, "Nq": wp.Nq, "Nk": wp.Nk, "d": wp.d, "dtype": "bf16", "causal": True}
+        if not (do_p or do_d):
+            out.update({"value": tb, "unit": "TFLOP/s", "dtype": "bf16"})
+            cfg["workload"] = "bwd on long_causal: B=1 H=32 Nq=Nk=8192 d=128 bf16 causal"
     if do_g:
         # bytes the method must move: Q, O (B*H*d each), K, V (B*H_kv*Nk*d each), LSE
         gb = 2 * (2 * wg.B * wg.H * wg.d + 2 * wg.B * wg.H_kv * wg.Nk * wg.d) + 4 * wg.B * wg.H

@@ -116,6 +116,27 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
     return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
+    const int64_t n = count4(B, H, Nq, 1);
+    if (n < 0 || n > INT64_MAX / 4) return 0;
+    return (size_t)n * 4u;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+    fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 15u) || ((uintptr_t)workspace & 15u))
+        return FA_ERR_UNSUPPORTED;
+    fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, Nk, d, causal != 0,
+                    dtype == FA_BF16, scale};
+    return from_hip(fa::launch_bwd(p, (hipStream_t)stream));
+}
+
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
     if (!supported_d(d) || num_splits < 1) return 0;
     const int64_t n = count4(num_splits, B, H, Nq);

@@ -1,0 +1,460 @@
+// fa_bwd.hip -- FlashAttention-2 backward on gfx950 MFMA: dQ, dK, dV from Q, K,
+// V, O, dO and the forward's LSE.
+//
+// Method (the pages this follows):
+//   * Recompute instead of storing P: each tile re-forms S = scale * Q K^T and
+//     P = exp(S - LSE) from the saved log-sum-exp (Ringi, "Lecture 25", section
+//     3.3; AIInfraGuide 6.2, forward pseudocode: the saved statistic is
+//     L = m + log l).
+//   * Gradients: dV = P^T dO, dP = dO V^T, dS = P o (dP - D) with
+//     D = rowsum(dP o P) = rowsum(dO o O), dQ = scale dS K, dK = scale dS^T Q
+//     (Ringi, section 3.3; the scale enters through S).
+//   * Parallelism: dK and dV of a key block collect every query that sees it, so
+//     a workgroup fixes a key block and walks the query tiles; dQ of a query
+//     block collects every key block, which the pages do with atomics or a
+//     deterministic scheme (LLM Infra Atlas, "FA2: parallelism", section 5).
+//     Here a second kernel fixes a query block and walks the key tiles, so no
+//     atomics are used and the result is deterministic.
+//
+// gfx950 mapping (not from the pages):
+//   * dQ kernel (the forward's layout): S^T = K Q^T and dP^T = V dO^T on
+//     v_mfma_f32_32x32x16 with Q and dO held in registers; K and V rows enter in
+//     the order with bits 2 and 3 swapped, so registers 8p..8p+7 of the
+//     accumulators are the 8 consecutive keys a lane supplies as the B operand
+//     of dQ^T += K^T dS^T, with K^T read through ds_read_b64_tr_b16.  One lane
+//     owns one query row: LSE and D are per-lane scalars.
+//   * dK/dV kernel (its transpose): each wave owns 32 keys held in registers;
+//     S = Q K^T and dP = dO V^T with Q and dO rows in the swapped order, so P and
+//     dS feed dV^T += dO^T P and dK^T += Q^T dS directly.  LSE and D of the
+//     tile's query rows sit in LDS next to the Q and dO tiles.
+//   * Rows past the end of Q read as zeros (so they add nothing to dK, dV), and
+//     keys past the end of K only reach their own, unstored, dK/dV columns; the
+//     dK/dV kernel therefore only applies the causal condition, as a select per
+//     score.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int BQ = 128;   // dQ kernel: query rows per workgroup (4 waves x 32)
+constexpr int BK = 64;    // dQ kernel: keys per tile
+constexpr int CK = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
+constexpr int CQ = 64;    // dK/dV kernel: query rows per tile
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    float* delta;        // D = rowsum(dO o O), [B, H, Nq]
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    int BH, Nq, Nk;
+    float c;             // scale * log2(e), sign included
+    float scale;
+    int n_qtiles;        // dQ kernel work items per head
+    int n_ktiles;        // dK/dV kernel work items per head
+};
+
+// Row index (within a 32-row block) that accumulator row i stands for: bits 2 and 3 swapped.
+__device__ __forceinline__ int perm_row(int i) {
+    return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// D_i = sum_t dO[i,t] O[i,t] in fp32, one thread per row.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    const uint16_t* op = a.o + (size_t)row * D;
+    const uint16_t* gp = a.dout + (size_t)row * D;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int t = 0; t < D; t += 8) {
+        const u32x4 ov = *(const u32x4*)(op + t);
+        const u32x4 gv = *(const u32x4*)(gp + t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(widen<BF16>((uint16_t)(ov[i] & 0xffff)), widen<BF16>((uint16_t)(gv[i] & 0xffff)), acc);
+            acc = __builtin_fmaf(widen<BF16>((uint16_t)(ov[i] >> 16)), widen<BF16>((uint16_t)(gv[i] >> 16)), acc);
+        }
+    }
+    a.delta[row] = acc;
+}
+
+// Per-lane LDS offsets shared by both kernels (tiles of rows of D 16-bit values,
+// XOR-swizzled): row reads of the A operand with rows in the swapped order, and
+// transposed reads of 4 rows x 4 chunks.
+template <int D>
+struct Offsets {
+    int row[D / 16];          // A operand: row perm_row(l32), chunk 2s + h
+    int tr[2][D / 32];        // transposed A operand: block db, half 0/1
+    __device__ __forceinline__ Offsets(int lane) {
+        const int l32 = lane & 31, h = lane >> 5;
+        const int r0 = perm_row(l32);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) row[s] = lds_off<D>(r0, 2 * s + h);
+        const int r4 = (lane & 15) >> 2, c4 = lane & 3, g1 = (lane >> 4) & 1;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                tr[half][db] = lds_off<D>(8 * h + r4 + 4 * half, 4 * db + 2 * g1 + (c4 >> 1)) + (c4 & 1) * 8;
+    }
+};
+
+// A operand of rows^T (d block db, 16 rows starting at `rows`) via transposed reads.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const unsigned char* rows, const Offsets<D>& of, int db) {
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(rows + of.tr[0][db]));
+    const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(rows + of.tr[1][db]));
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Fill `nload` 1 KiB chunks of an LDS tile of rows (the wave's share) from
+// global rows through buffer loads that write LDS; rows past the descriptor's
+// record count read as zeros.
+template <int D, int NPW>
+__device__ __forceinline__ void load_rows(const uint16_t* base, int rows_left, unsigned char* dst_tile, int w,
+                                          const u32 (&voff)[NPW]) {
+    const u32 nrec = (u32)min(max(rows_left, 0), 64) * (D * 2);   // tiles hold 64 rows
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base, nrec);
+    unsigned char* dst = dst_tile + w * NPW * 1024;
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
+}
+
+template <int D, int NPW>
+__device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW]) {
+    constexpr int ROWB = D * 2;
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+        const int pos = (w * NPW + u) * 1024 + lane * 16;
+        const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
+        voff[u] = (u32)(row * ROWB + ((pchunk ^ swz<D>(row)) << 4));
+    }
+}
+
+// Work item from blockIdx: XCD-contiguous ranges (tiles of one head share an
+// XCD's L2), `per_head` tiles per head, tile index in the order given.
+__device__ __forceinline__ void work_item(int per_head, int BH, int& tile, int& bh) {
+    const int total = gridDim.x;
+    int L = blockIdx.x;
+    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    tile = L % per_head;
+    bh = (L / per_head) % BH;
+}
+
+// ---- dQ ---------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int ROWB = D * 2, TILE = BK * ROWB, NS = D / 16, ND = D / 32;
+    constexpr int NPW = TILE / 1024 / 4;
+    __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];   // [K | V]
+    __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
+
+    int t, bh;
+    work_item(a.n_qtiles, a.BH, t, bh);
+    const int qt = a.n_qtiles - 1 - t;                   // longest causal rows first
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+    const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
+    const uint16_t* kg = a.k + (size_t)bh * Nk * D;
+    const uint16_t* vg = a.v + (size_t)bh * Nk * D;
+
+    int hi = Nk;
+    if (CAUSAL) hi = min(hi, min(Nq, q0 + BQ) + off);
+    const int n_tiles = hi > 0 ? (hi + BK - 1) / BK : 0;
+
+    // this lane's query row: Q and dO chunks, LSE (log2 units) and D
+    u32x4 qf[NS], gf[NS];
+    const bool qok = qi < Nq;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const size_t e = ((size_t)bh * Nq + qi) * D + 16 * s + 8 * h;
+        qf[s] = qok ? *(const u32x4*)(a.q + e) : u32x4{0, 0, 0, 0};
+        gf[s] = qok ? *(const u32x4*)(a.dout + e) : u32x4{0, 0, 0, 0};
+    }
+    const float lse2 = qok ? a.lse[(size_t)bh * Nq + qi] * kLog2e : 0.f;
+    const float dlt = qok ? a.delta[(size_t)bh * Nq + qi] : 0.f;
+
+    u32 voff[NPW];
+    dma_offsets<D, NPW>(w, lane, voff);
+    auto load_tile = [&](int tile, unsigned char* stage) {
+        const int k0 = tile * BK;
+        load_rows<D, NPW>(kg + (size_t)k0 * D, Nk - k0, stage, w, voff);
+        load_rows<D, NPW>(vg + (size_t)k0 * D, Nk - k0, stage + TILE, w, voff);
+    };
+    const Offsets<D> of(lane);
+
+    f32x16 dqacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) dqacc[db] = f32x16{};
+
+    // One key tile.  Keys at or past `bound` (relative to k0 + 8h; the key tail
+    // or, causal, past this row's diagonal) get P = 0; clean tiles pass a bound
+    // past the tile.
+    auto step = [&](const unsigned char* Kb, const unsigned char* Vb, int bound) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                sacc = mfma32<BF16>(*(const u32x4*)(Kb + 32 * kb * ROWB + of.row[s]), qf[s], sacc);
+                pacc = mfma32<BF16>(*(const u32x4*)(Vb + 32 * kb * ROWB + of.row[s]), gf[s], pacc);
+            }
+            // register 8p + e stands for key k0 + 32kb + 16p + 8h + e
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                float ds[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float pr = exp2_fast(__builtin_fmaf(sacc[8 * p + e], a.c, -lse2));
+                    pr = (32 * kb + 16 * p + e < bound) ? pr : 0.f;
+                    ds[e] = pr * (pacc[8 * p + e] - dlt);
+                }
+                const u32x4 dsb = {pack2<BF16>(ds[0], ds[1]), pack2<BF16>(ds[2], ds[3]),
+                                   pack2<BF16>(ds[4], ds[5]), pack2<BF16>(ds[6], ds[7])};
+                const unsigned char* kr = Kb + (32 * kb + 16 * p) * ROWB;
+#pragma unroll
+                for (int db = 0; db < ND; ++db) dqacc[db] = mfma32<BF16>(tr_operand<D>(kr, of, db), dsb, dqacc[db]);
+            }
+        }
+    };
+
+    // key tiles from the last one down: the ones crossing the diagonal or the key
+    // tail come first
+    int n_masked = 0;
+    while (n_masked < n_tiles) {
+        const int k0 = (n_tiles - 1 - n_masked) * BK;
+        const bool clean = k0 + BK <= Nk && (!CAUSAL || k0 + BK - 1 <= q0 + off);
+        if (clean) break;
+        ++n_masked;
+    }
+    if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int it = 0;
+#pragma clang loop unroll(disable)
+    for (; it < n_tiles; ++it) {
+        const int tile = n_tiles - 1 - it;
+        unsigned char* cur = (it & 1) ? stage1 : stage0;
+        unsigned char* nxt = (it & 1) ? stage0 : stage1;
+        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+        const int k0 = tile * BK;
+        if (it < n_masked) {
+            if (qw < Nq && (!CAUSAL || k0 <= min(qw + 31, Nq - 1) + off)) {
+                int bound = Nk - k0;
+                if (CAUSAL) bound = min(bound, qi + off - k0 + 1);
+                step(cur, cur + TILE, bound - 8 * h);
+            }
+        } else {
+            step(cur, cur + TILE, BK);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    if (qok) {
+        uint16_t* dst = a.dq + ((size_t)bh * Nq + qi) * D;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
+                const u32x2 v2 = {pack2<BF16>(x[0] * a.scale, x[1] * a.scale), pack2<BF16>(x[2] * a.scale, x[3] * a.scale)};
+                *(u32x2*)(dst + 32 * db + 8 * g + 4 * h) = v2;
+            }
+    }
+}
+
+// ---- dK, dV -------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+    constexpr int ROWB = D * 2, QTILE = CQ * ROWB, NS = D / 16, ND = D / 32;
+    constexpr int NPW = QTILE / 1024 / 4;
+    constexpr int STAGE = 2 * QTILE + 2048;             // [Q | dO | LSE (1 KiB) | D (1 KiB)]
+    __shared__ __attribute__((aligned(16))) unsigned char stage0[STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char stage1[STAGE];
+
+    int kt, bh;
+    work_item(a.n_ktiles, a.BH, kt, bh);                // key tile 0 first: the longest causal columns
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+    const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
+    const uint16_t* qg = a.q + (size_t)bh * Nq * D;
+    const uint16_t* gg = a.dout + (size_t)bh * Nq * D;
+    const float* lg = a.lse + (size_t)bh * Nq;
+    const float* dg = a.delta + (size_t)bh * Nq;
+
+    // first query row that sees a key of this block, and the query tiles from it
+    const int q_lo = CAUSAL ? max(0, k0 - off) : 0;
+    const int t0 = q_lo / CQ;
+    const int n_qt = (Nq + CQ - 1) / CQ;
+    const int n_tiles = q_lo < Nq ? n_qt - t0 : 0;
+
+    // this lane's key row: K and V chunks (the B operands)
+    u32x4 kf[NS], vf[NS];
+    const bool kok = kj < Nk;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const size_t e = ((size_t)bh * Nk + kj) * D + 16 * s + 8 * h;
+        kf[s] = kok ? *(const u32x4*)(a.k + e) : u32x4{0, 0, 0, 0};
+        vf[s] = kok ? *(const u32x4*)(a.v + e) : u32x4{0, 0, 0, 0};
+    }
+
+    u32 voff[NPW];
+    dma_offsets<D, NPW>(w, lane, voff);
+    auto load_tile = [&](int tile, unsigned char* stage) {
+        const int i0 = tile * CQ;
+        load_rows<D, NPW>(qg + (size_t)i0 * D, Nq - i0, stage, w, voff);
+        load_rows<D, NPW>(gg + (size_t)i0 * D, Nq - i0, stage + QTILE, w, voff);
+        // 64 LSE and 64 D values (256 B each) land at lane*16 of a 1 KiB area;
+        // lanes past 64 rows read zeros
+        const u32 nrec = (u32)min(max(Nq - i0, 0), CQ) * 4;
+        if (w == 0) lds_dma16(buffer_rsrc(lg + i0, nrec), stage + 2 * QTILE, (u32)lane * 16);
+        if (w == 1) lds_dma16(buffer_rsrc(dg + i0, nrec), stage + 2 * QTILE + 1024, (u32)lane * 16);
+    };
+    const Offsets<D> of(lane);
+
+    f32x16 dkacc[ND], dvacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        dkacc[db] = f32x16{};
+        dvacc[db] = f32x16{};
+    }
+
+    // One query tile.  Causal: keys after a row's diagonal get P = 0 (also in
+    // tiles fully past the diagonal, where the test never fires).
+    auto step = [&](const unsigned char* st, int i0) {
+        const unsigned char* Qb = st;
+        const unsigned char* Gb = st + QTILE;
+        const float* Ls = (const float*)(st + 2 * QTILE);
+        const float* Ds = (const float*)(st + 2 * QTILE + 1024);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                sacc = mfma32<BF16>(*(const u32x4*)(Qb + 32 * kb * ROWB + of.row[s]), kf[s], sacc);
+                pacc = mfma32<BF16>(*(const u32x4*)(Gb + 32 * kb * ROWB + of.row[s]), vf[s], pacc);
+            }
+            // register 8p + e stands for query row i0 + 32kb + 16p + 8h + e
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int rb = 32 * kb + 16 * p + 8 * h;
+                const f32x4 la = *(const f32x4*)(Ls + rb), lb = *(const f32x4*)(Ls + rb + 4);
+                const f32x4 da = *(const f32x4*)(Ds + rb), dbv = *(const f32x4*)(Ds + rb + 4);
+                const float lr[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+                const float dr[8] = {da[0], da[1], da[2], da[3], dbv[0], dbv[1], dbv[2], dbv[3]};
+                float pr[8], ds[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pr[e] = exp2_fast(__builtin_fmaf(sacc[8 * p + e], a.c, -lr[e] * kLog2e));
+                    if (CAUSAL) pr[e] = (kj <= i0 + rb + e + off) ? pr[e] : 0.f;
+                    ds[e] = pr[e] * (pacc[8 * p + e] - dr[e]);
+                }
+                const u32x4 pb = {pack2<BF16>(pr[0], pr[1]), pack2<BF16>(pr[2], pr[3]),
+                                  pack2<BF16>(pr[4], pr[5]), pack2<BF16>(pr[6], pr[7])};
+                const u32x4 sb = {pack2<BF16>(ds[0], ds[1]), pack2<BF16>(ds[2], ds[3]),
+                                  pack2<BF16>(ds[4], ds[5]), pack2<BF16>(ds[6], ds[7])};
+                const unsigned char* qr = Qb + (32 * kb + 16 * p) * ROWB;
+                const unsigned char* gr = Gb + (32 * kb + 16 * p) * ROWB;
+#pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    dvacc[db] = mfma32<BF16>(tr_operand<D>(gr, of, db), pb, dvacc[db]);
+                    dkacc[db] = mfma32<BF16>(tr_operand<D>(qr, of, db), sb, dkacc[db]);
+                }
+            }
+        }
+    };
+
+    // query tiles upward from the diagonal: the first ones may hold rows that do
+    // not yet see some keys of the block
+    if (n_tiles > 0) load_tile(t0, stage0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma clang loop unroll(disable)
+    for (int it = 0; it < n_tiles; ++it) {
+        const int tile = t0 + it;
+        unsigned char* cur = (it & 1) ? stage1 : stage0;
+        unsigned char* nxt = (it & 1) ? stage0 : stage1;
+        if (it + 1 < n_tiles) load_tile(tile + 1, nxt);
+        const int i0 = tile * CQ;
+        // skip a wave whose keys no row of the tile sees yet
+        if (!CAUSAL || kw <= i0 + CQ - 1 + off) step(cur, i0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    if (kok) {
+        uint16_t* dkp = a.dk + ((size_t)bh * Nk + kj) * D;
+        uint16_t* dvp = a.dv + ((size_t)bh * Nk + kj) * D;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = 32 * db + 8 * g + 4 * h;
+                const u32x2 k2 = {pack2<BF16>(dkacc[db][4 * g] * a.scale, dkacc[db][4 * g + 1] * a.scale),
+                                  pack2<BF16>(dkacc[db][4 * g + 2] * a.scale, dkacc[db][4 * g + 3] * a.scale)};
+                const u32x2 v2 = {pack2<BF16>(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
+                                  pack2<BF16>(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
+                *(u32x2*)(dkp + c0) = k2;
+                *(u32x2*)(dvp + c0) = v2;
+            }
+    }
+}
+
+template <bool BF16, int D>
+hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
+    const int64_t dblocks = (rows + 255) / 256;
+    hipLaunchKernelGGL((bwd_delta_kernel<BF16, D>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
+    const int kv_blocks = a.n_ktiles * a.BH, q_blocks = a.n_qtiles * a.BH;
+    if (causal) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true>), dim3(kv_blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true>), dim3(q_blocks), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, false>), dim3(kv_blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false>), dim3(q_blocks), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+    BwdArgs a;
+    a.q = (const uint16_t*)p.q;
+    a.k = (const uint16_t*)p.k;
+    a.v = (const uint16_t*)p.v;
+    a.o = (const uint16_t*)p.o;
+    a.dout = (const uint16_t*)p.dout;
+    a.lse = p.lse;
+    a.delta = p.delta;
+    a.dq = (uint16_t*)p.dq;
+    a.dk = (uint16_t*)p.dk;
+    a.dv = (uint16_t*)p.dv;
+    a.BH = p.B * p.H;
+    a.Nq = p.Nq;
+    a.Nk = p.Nk;
+    a.c = p.scale * kLog2e;
+    a.scale = p.scale;
+    a.n_qtiles = (p.Nq + BQ - 1) / BQ;
+    a.n_ktiles = (p.Nk + CK - 1) / CK;
+    const int64_t rows = (int64_t)a.BH * p.Nq;
+    if ((int64_t)a.n_qtiles * a.BH > 0x7fffffff || (int64_t)a.n_ktiles * a.BH > 0x7fffffff ||
+        (rows + 255) / 256 > 0x7fffffff)
+        return hipErrorInvalidValue;
+    if (p.d == 128) return p.bf16 ? launch_bwd_t<true, 128>(a, p.causal, rows, stream)
+                                  : launch_bwd_t<false, 128>(a, p.causal, rows, stream);
+    return p.bf16 ? launch_bwd_t<true, 64>(a, p.causal, rows, stream)
+                  : launch_bwd_t<false, 64>(a, p.causal, rows, stream);
+}
+
+}  // namespace fa

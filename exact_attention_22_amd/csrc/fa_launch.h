@@ -28,7 +28,27 @@ struct FwdParams {
     int total_q, total_k;
 };
 
+// Validated arguments of one backward launch ([B, H, N, d] tensors; delta is
+// the caller's fp32 workspace of B * H * Nq values).
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;
+    int B, H, Nq, Nk, d;
+    bool causal;
+    bool bf16;
+    float scale;
+};
+
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_decode(const FwdParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                           int64_t rows, int d, int num_splits, bool bf16, hipStream_t stream);

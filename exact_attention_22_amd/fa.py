@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
-           "fa_fwd_splitkv_gqa", "fa_splitkv_combine", "fa_status_str")
+           "fa_fwd_splitkv_gqa", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -50,6 +50,10 @@ def lib():
         L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         L.fa_splitkv_combine.restype = i
         L.fa_splitkv_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+        L.fa_bwd.restype = i
+        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, f, i, vp]
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [i]
         _lib = L
@@ -223,6 +227,34 @@ def splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, stream=None):
     lp = _dev_tensor(lse, "lse", torch.float32)
     _check(lib().fa_splitkv_combine(opp, lpp, op, lp, B, H, Nq, d, S, _DTYPES[dtype], _stream(stream)))
     return out, lse
+
+
+def bwd_workspace_bytes(B, H, Nq):
+    return int(lib().fa_bwd_workspace_bytes(B, H, Nq))
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+        stream=None):
+    """dQ, dK, dV for the upstream gradient dout, from the forward's inputs, o and lse."""
+    (qp, kp, vp), (B, H, Nq, Nk, d) = _qkv(q, k, v)
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o and dout must be [B, H, Nq, d] and lse [B, H, Nq]")
+    opp = _dev_tensor(o, "o", q.dtype)
+    gp = _dev_tensor(dout, "dout", q.dtype)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(v.shape):
+        raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    nbytes = bwd_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    wp = _dev_tensor(workspace, "workspace")
+    ptrs = [_dev_tensor(t, n, q.dtype) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _check(lib().fa_bwd(qp, kp, vp, opp, gp, lp, *ptrs, wp, workspace.numel() * workspace.element_size(),
+                        B, H, Nq, Nk, d, int(bool(causal)), _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
+    return dq, dk, dv
 
 
 def decode(q, k, v, num_splits=16, causal=False, scale=None, stream=None, o_part=None, lse_part=None):

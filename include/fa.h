@@ -57,7 +57,7 @@ typedef enum {
     FA_ERR_SHAPE = 2,       /* B, H, Nq, Nk < 1, num_splits out of [1, Nk], H_kv not dividing H,
                                or a size overflows */
     FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite scale, misaligned pointer */
-    FA_ERR_WORKSPACE = 4,   /* reserved: a workspace too small for the request */
+    FA_ERR_WORKSPACE = 4,   /* a workspace too small for the request */
     FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
 } fa_status;
 
@@ -157,6 +157,32 @@ fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v,
 fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                              int B, int H, int Nq, int d, int num_splits,
                              fa_dtype dtype, void* stream);
+
+/*
+ * Bytes of fp32 workspace fa_bwd needs: B * H * Nq * 4 (one value per query
+ * row).  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
+
+/*
+ * Backward pass: gradients dq, dk, dv ([B,H,N,d], dtype) of a loss whose
+ * gradient with respect to o is dout, given the forward's inputs, its output o
+ * and its lse.  P is recomputed tile by tile from the saved log-sum-exp instead
+ * of being stored (Ringi, Lecture 25, section 3.3):
+ *   dV = P^T dO;  dP = dO V^T;  dS = P o (dP - rowsum(dP o P));
+ *   dQ = scale * dS K;  dK = scale * dS^T Q
+ * rowsum(dP o P) equals rowsum(dO o O); the library computes it that way into
+ * `workspace` (fp32, at least fa_bwd_workspace_bytes; its contents on entry do
+ * not matter).  dK and dV are accumulated per key block over the query tiles and
+ * dQ per query block over the key tiles, so no atomics are used and the results
+ * are deterministic (LLM Infra Atlas, FA2 parallelism, section 5).  Same
+ * conventions as fa_fwd (causal alignment, scale, rounding); lse and workspace
+ * must be 16-byte aligned.  A workspace smaller than required returns
+ * FA_ERR_WORKSPACE.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);

@@ -44,3 +44,28 @@ def sample_rows(B, H, Nq, n_random=256, seed=0):
     if Nq > 1:
         rows.append(bh * Nq + 1)
     return np.unique(np.concatenate(rows))
+
+
+# Gradients: max |g - g_oracle| / max |g_oracle| per tensor.  The backward rounds
+# P and dS to the input type before its products, reads the forward's rounded O
+# and rounds its outputs, each a relative error of at most the unit roundoff u
+# (2^-11 fp16, 2^-8 bf16); the bar is 4u of the largest gradient.
+GRAD_TOL = {torch.float16: 4 * 2.0 ** -11, torch.bfloat16: 4 * 2.0 ** -8}
+
+
+def grad_errors(grads, refs):
+    out = {}
+    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        a = g.detach().double().cpu().numpy().reshape(r.shape)
+        assert not np.isnan(a).any(), f"NaN in {name}"
+        scale = max(float(np.max(np.abs(r), initial=0.0)), 1e-30)
+        out[name] = float(np.max(np.abs(a - r), initial=0.0)) / scale
+    return out
+
+
+def check_grads(grads, refs, dtype, what=""):
+    e = grad_errors(grads, refs)
+    print(f"[parity] {what} {e}", flush=True)
+    for name, err in e.items():
+        assert err <= GRAD_TOL[dtype], f"{what}: {name} normalised error {err:.3e}"
+    return e

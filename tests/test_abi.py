@@ -86,6 +86,25 @@ def test_gqa_validation():
     assert split_gqa(q=MIS) == fa.FA_ERR_UNSUPPORTED
 
 
+def bwd(q=A, k=A, v=A, o=A, g=A, lse=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 20, B=1, H=2, Nq=64, Nk=64, d=128,
+        causal=1, scale=0.1, dtype=1):
+    return fa.lib().fa_bwd(q, k, v, o, g, lse, dq, dk, dv, ws, wsb, B, H, Nq, Nk, d, causal, scale, dtype, NULL)
+
+
+def test_bwd_validation():
+    assert fa.bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+    assert fa.bwd_workspace_bytes(0, 3, 5) == 0
+    assert bwd(g=NULL) == fa.FA_ERR_NULL
+    assert bwd(ws=NULL) == fa.FA_ERR_NULL
+    assert bwd(dv=NULL) == fa.FA_ERR_NULL
+    assert bwd(wsb=2 * 64 * 4 - 4) == fa.FA_ERR_WORKSPACE
+    assert bwd(Nk=0) == fa.FA_ERR_SHAPE
+    assert bwd(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(scale=float("inf")) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(dq=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lse=MIS) == fa.FA_ERR_UNSUPPORTED
+
+
 def varlen(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, B=2, H=4, H_kv=2, total_q=16, total_k=24, max_q=9,
            max_k=13, d=128, causal=1, scale=0.1, dtype=1):
     return fa.lib().fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, H_kv, total_q, total_k, max_q, max_k,
