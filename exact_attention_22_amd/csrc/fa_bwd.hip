@@ -153,7 +153,7 @@ __device__ __forceinline__ void work_item(int per_head, int BH, int& tile, int& 
 
 // ---- dQ ---------------------------------------------------------------------
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     constexpr int ROWB = D * 2, TILE = BK * ROWB, NS = D / 16, ND = D / 32;
     constexpr int NPW = TILE / 1024 / 4;
     __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];   // [K | V]
@@ -240,12 +240,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    int it = 0;
-#pragma clang loop unroll(disable)
-    for (; it < n_tiles; ++it) {
+    // two tiles per trip, so that each step reads one fixed LDS stage
+    auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
         const int tile = n_tiles - 1 - it;
-        unsigned char* cur = (it & 1) ? stage1 : stage0;
-        unsigned char* nxt = (it & 1) ? stage0 : stage1;
         if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
         const int k0 = tile * BK;
         if (it < n_masked) {
@@ -259,6 +256,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+#pragma clang loop unroll(disable)
+    for (int it = 0; it < n_tiles; it += 2) {
+        one(it, stage0, stage1);
+        if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
     }
 
     if (qok) {
@@ -380,17 +382,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (n_tiles > 0) load_tile(t0, stage0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma clang loop unroll(disable)
-    for (int it = 0; it < n_tiles; ++it) {
+    // two tiles per trip, so that each step reads one fixed LDS stage
+    auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
         const int tile = t0 + it;
-        unsigned char* cur = (it & 1) ? stage1 : stage0;
-        unsigned char* nxt = (it & 1) ? stage0 : stage1;
         if (it + 1 < n_tiles) load_tile(tile + 1, nxt);
         const int i0 = tile * CQ;
         // skip a wave whose keys no row of the tile sees yet
         if (!CAUSAL || kw <= i0 + CQ - 1 + off) step(cur, i0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+#pragma clang loop unroll(disable)
+    for (int it = 0; it < n_tiles; it += 2) {
+        one(it, stage0, stage1);
+        if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
     }
 
     if (kok) {
