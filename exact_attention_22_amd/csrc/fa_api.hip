@@ -118,8 +118,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
     const int64_t n = count4(B, H, Nq, 1);
-    if (n < 0 || n > INT64_MAX / 4) return 0;
-    return (size_t)n * 4u;
+    if (n < 0 || n > INT64_MAX / 8) return 0;
+    return (size_t)n * 8u;   // D and LSE * log2(e), fp32 each
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -25,12 +25,14 @@
 //     owns one query row: LSE and D are per-lane scalars.
 //   * dK/dV kernel (its transpose): each wave owns 32 keys held in registers;
 //     S = Q K^T and dP = dO V^T with Q and dO rows in the swapped order, so P and
-//     dS feed dV^T += dO^T P and dK^T += Q^T dS directly.  LSE and D of the
-//     tile's query rows sit in LDS next to the Q and dO tiles.
+//     dS feed dV^T += dO^T P and dK^T += Q^T dS directly.  LSE (in base 2) and
+//     D of the tile's query rows sit in LDS next to the Q and dO tiles.  At one
+//     wave per SIMD the wave overlaps its own work: the scores of a tile's second
+//     32-row block are issued before the first block's element-wise work.
 //   * Rows past the end of Q read as zeros (so they add nothing to dK, dV), and
 //     keys past the end of K only reach their own, unstored, dK/dV columns; the
 //     dK/dV kernel therefore only applies the causal condition, as a select per
-//     score.
+//     score in the tiles that cross a wave's diagonal.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -52,6 +54,7 @@ struct BwdArgs {
     const uint16_t* dout;
     const float* lse;
     float* delta;        // D = rowsum(dO o O), [B, H, Nq]
+    float* lse2;         // LSE * log2(e), [B, H, Nq]
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -67,7 +70,7 @@ __device__ __forceinline__ int perm_row(int i) {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// D_i = sum_t dO[i,t] O[i,t] in fp32, one thread per row.
+// D_i = sum_t dO[i,t] O[i,t] in fp32, and LSE_i * log2(e), one thread per row.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -86,6 +89,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t rows)
         }
     }
     a.delta[row] = acc;
+    a.lse2[row] = a.lse[row] * kLog2e;
 }
 
 // Per-lane LDS offsets shared by both kernels (tiles of rows of D 16-bit values,
@@ -123,7 +127,9 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned char* rows, const Off
 template <int D, int NPW>
 __device__ __forceinline__ void load_rows(const uint16_t* base, int rows_left, unsigned char* dst_tile, int w,
                                           const u32 (&voff)[NPW]) {
-    const u32 nrec = (u32)min(max(rows_left, 0), 64) * (D * 2);   // tiles hold 64 rows
+    // wave-uniform record count (a per-lane value would wrap each load in a
+    // readfirstlane loop)
+    const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(rows_left, 0), 64)) * (D * 2);   // tiles hold 64 rows
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base, nrec);
     unsigned char* dst = dst_tile + w * NPW * 1024;
 #pragma unroll
@@ -151,7 +157,64 @@ __device__ __forceinline__ void work_item(int per_head, int BH, int& tile, int& 
     bh = (L / per_head) % BH;
 }
 
+// Two score products over one 32-row block of LDS tiles: S = A1 B1 and
+// P' = A2 B2, with A1, A2 the rows 32kb.. of tiles T1, T2 (in the swapped order)
+// and B1, B2 the lane's register-resident operands.  dK/dV kernel: S = Q K^T,
+// dP = dO V^T; dQ kernel: S^T = K Q^T, dP^T = V dO^T.
+template <bool BF16, int D>
+__device__ __forceinline__ void scores(const unsigned char* T1, const unsigned char* T2, int kb,
+                                       const Offsets<D>& of, const u32x4 (&b1)[D / 16],
+                                       const u32x4 (&b2)[D / 16], f32x16& s, f32x16& dp) {
+    constexpr int NS = D / 16, ROWB = D * 2;
+    u32x4 a1[NS], a2[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        a1[i] = *(const u32x4*)(T1 + 32 * kb * ROWB + of.row[i]);
+        a2[i] = *(const u32x4*)(T2 + 32 * kb * ROWB + of.row[i]);
+    }
+    s = mfma32<BF16>(a1[0], b1[0], f32x16{});
+    dp = mfma32<BF16>(a2[0], b2[0], f32x16{});
+#pragma unroll
+    for (int i = 1; i < NS; ++i) {
+        s = mfma32<BF16>(a1[i], b1[i], s);
+        dp = mfma32<BF16>(a2[i], b2[i], dp);
+    }
+}
+
 // ---- dQ ---------------------------------------------------------------------
+// dS^T for one 32-key block (register 8p + e stands for key k0 + 32kb + 16p + 8h
+// + e), packed as the B operand of dQ^T += K^T dS^T.  MASK zeroes P from key
+// 16p + e >= bound on (the key tail, or keys past this row's diagonal).
+template <bool BF16, bool MASK>
+__device__ __forceinline__ void dq_probs(const f32x16& s, const f32x16& dp, float lse2, float dlt, float c,
+                                         int bound, u32x4 (&dsb)[2]) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float pr = exp2_fast(__builtin_fmaf(s[8 * p + e], c, -lse2));
+            if (MASK) pr = (16 * p + e < bound) ? pr : 0.f;
+            ds[e] = pr * (dp[8 * p + e] - dlt);
+        }
+        dsb[p] = u32x4{pack2<BF16>(ds[0], ds[1]), pack2<BF16>(ds[2], ds[3]), pack2<BF16>(ds[4], ds[5]),
+                       pack2<BF16>(ds[6], ds[7])};
+    }
+}
+
+// dQ^T += K^T dS^T over the keys of that block, K^T through transposed reads.
+template <bool BF16, int D>
+__device__ __forceinline__ void dq_accum(const unsigned char* Kb, int kb, const Offsets<D>& of,
+                                         const u32x4 (&dsb)[2], f32x16 (&dq)[D / 32]) {
+    constexpr int ROWB = D * 2;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const unsigned char* kr = Kb + (32 * kb + 16 * p) * ROWB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dq[db] = mfma32<BF16>(tr_operand<D>(kr, of, db), dsb[p], dq[db]);
+    }
+}
+
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     constexpr int ROWB = D * 2, TILE = BK * ROWB, NS = D / 16, ND = D / 32;
@@ -162,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     int t, bh;
     work_item(a.n_qtiles, a.BH, t, bh);
     const int qt = a.n_qtiles - 1 - t;                   // longest causal rows first
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
     const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
     const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
     const uint16_t* kg = a.k + (size_t)bh * Nk * D;
@@ -181,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         qf[s] = qok ? *(const u32x4*)(a.q + e) : u32x4{0, 0, 0, 0};
         gf[s] = qok ? *(const u32x4*)(a.dout + e) : u32x4{0, 0, 0, 0};
     }
-    const float lse2 = qok ? a.lse[(size_t)bh * Nq + qi] * kLog2e : 0.f;
+    const float lse2 = qok ? a.lse2[(size_t)bh * Nq + qi] : 0.f;
     const float dlt = qok ? a.delta[(size_t)bh * Nq + qi] : 0.f;
 
     u32 voff[NPW];
@@ -197,35 +260,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < ND; ++db) dqacc[db] = f32x16{};
 
-    // One key tile.  Keys at or past `bound` (relative to k0 + 8h; the key tail
-    // or, causal, past this row's diagonal) get P = 0; clean tiles pass a bound
-    // past the tile.
-    auto step = [&](const unsigned char* Kb, const unsigned char* Vb, int bound) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                sacc = mfma32<BF16>(*(const u32x4*)(Kb + 32 * kb * ROWB + of.row[s]), qf[s], sacc);
-                pacc = mfma32<BF16>(*(const u32x4*)(Vb + 32 * kb * ROWB + of.row[s]), gf[s], pacc);
-            }
-            // register 8p + e stands for key k0 + 32kb + 16p + 8h + e
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                float ds[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float pr = exp2_fast(__builtin_fmaf(sacc[8 * p + e], a.c, -lse2));
-                    pr = (32 * kb + 16 * p + e < bound) ? pr : 0.f;
-                    ds[e] = pr * (pacc[8 * p + e] - dlt);
-                }
-                const u32x4 dsb = {pack2<BF16>(ds[0], ds[1]), pack2<BF16>(ds[2], ds[3]),
-                                   pack2<BF16>(ds[4], ds[5]), pack2<BF16>(ds[6], ds[7])};
-                const unsigned char* kr = Kb + (32 * kb + 16 * p) * ROWB;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) dqacc[db] = mfma32<BF16>(tr_operand<D>(kr, of, db), dsb, dqacc[db]);
-            }
-        }
+    // One key tile of two 32-key blocks.  Keys at or past `bound` (relative to
+    // k0 + 8h; the key tail or, causal, past this row's diagonal) get P = 0 in
+    // masked tiles.  The scores of the second block are issued before the first
+    // block's element-wise work.
+    auto step = [&](const unsigned char* Kb, const unsigned char* Vb, int bound, auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
+        f32x16 s0, d0, s1, d1;
+        u32x4 ds0[2], ds1[2];
+        scores<BF16, D>(Kb, Vb, 0, of, qf, gf, s0, d0);
+        scores<BF16, D>(Kb, Vb, 1, of, qf, gf, s1, d1);
+        dq_probs<BF16, MASK>(s0, d0, lse2, dlt, a.c, bound, ds0);
+        dq_accum<BF16, D>(Kb, 0, of, ds0, dqacc);
+        dq_probs<BF16, MASK>(s1, d1, lse2, dlt, a.c, bound - 32, ds1);
+        dq_accum<BF16, D>(Kb, 1, of, ds1, dqacc);
     };
 
     // key tiles from the last one down: the ones crossing the diagonal or the key
@@ -249,10 +297,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             if (qw < Nq && (!CAUSAL || k0 <= min(qw + 31, Nq - 1) + off)) {
                 int bound = Nk - k0;
                 if (CAUSAL) bound = min(bound, qi + off - k0 + 1);
-                step(cur, cur + TILE, bound - 8 * h);
+                step(cur, cur + TILE, bound - 8 * h, std::true_type{});
             }
         } else {
-            step(cur, cur + TILE, BK);
+            step(cur, cur + TILE, BK, std::false_type{});
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -277,22 +325,67 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---- dK, dV -------------------------------------------------------------------
+// P = exp(S - LSE) and dS = P o (dP - D) for those rows, packed as the B operands
+// of the dV and dK products; register 8p + e stands for query row
+// 32kb + 16p + 8h + e (`rb` = 32kb + 8h).  Ls holds LSE * log2(e).  MASK zeroes
+// P where 16p + e < lim: rows that do not yet see this lane's key.
+template <bool BF16, bool MASK>
+__device__ __forceinline__ void dkdv_probs(const f32x16& s, const f32x16& dp, const float* Ls, const float* Ds,
+                                           int rb, float c, int lim, u32x4 (&pb)[2], u32x4 (&sb)[2]) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const f32x4 la = *(const f32x4*)(Ls + rb + 16 * p), lb = *(const f32x4*)(Ls + rb + 16 * p + 4);
+        const f32x4 da = *(const f32x4*)(Ds + rb + 16 * p), dbv = *(const f32x4*)(Ds + rb + 16 * p + 4);
+        const float lr[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+        const float dr[8] = {da[0], da[1], da[2], da[3], dbv[0], dbv[1], dbv[2], dbv[3]};
+        float pr[8], ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = exp2_fast(__builtin_fmaf(s[8 * p + e], c, -lr[e]));
+            if (MASK) pr[e] = (16 * p + e < lim) ? 0.f : pr[e];
+            ds[e] = pr[e] * (dp[8 * p + e] - dr[e]);
+        }
+        pb[p] = u32x4{pack2<BF16>(pr[0], pr[1]), pack2<BF16>(pr[2], pr[3]), pack2<BF16>(pr[4], pr[5]),
+                      pack2<BF16>(pr[6], pr[7])};
+        sb[p] = u32x4{pack2<BF16>(ds[0], ds[1]), pack2<BF16>(ds[2], ds[3]), pack2<BF16>(ds[4], ds[5]),
+                      pack2<BF16>(ds[6], ds[7])};
+    }
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS over those 32 rows.
+template <bool BF16, int D>
+__device__ __forceinline__ void dkdv_accum(const unsigned char* Qb, const unsigned char* Gb, int kb,
+                                           const Offsets<D>& of, const u32x4 (&pb)[2], const u32x4 (&sb)[2],
+                                           f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    constexpr int ROWB = D * 2;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const unsigned char* qr = Qb + (32 * kb + 16 * p) * ROWB;
+        const unsigned char* gr = Gb + (32 * kb + 16 * p) * ROWB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            dv[db] = mfma32<BF16>(tr_operand<D>(gr, of, db), pb[p], dv[db]);
+            dk[db] = mfma32<BF16>(tr_operand<D>(qr, of, db), sb[p], dk[db]);
+        }
+    }
+}
+
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int ROWB = D * 2, QTILE = CQ * ROWB, NS = D / 16, ND = D / 32;
     constexpr int NPW = QTILE / 1024 / 4;
-    constexpr int STAGE = 2 * QTILE + 2048;             // [Q | dO | LSE (1 KiB) | D (1 KiB)]
+    constexpr int STAGE = 2 * QTILE + 2048;             // [Q | dO | LSE*log2e (1 KiB) | D (1 KiB)]
     __shared__ __attribute__((aligned(16))) unsigned char stage0[STAGE];
     __shared__ __attribute__((aligned(16))) unsigned char stage1[STAGE];
 
     int kt, bh;
     work_item(a.n_ktiles, a.BH, kt, bh);                // key tile 0 first: the longest causal columns
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
     const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
     const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
     const uint16_t* qg = a.q + (size_t)bh * Nq * D;
     const uint16_t* gg = a.dout + (size_t)bh * Nq * D;
-    const float* lg = a.lse + (size_t)bh * Nq;
+    const float* lg = a.lse2 + (size_t)bh * Nq;
     const float* dg = a.delta + (size_t)bh * Nq;
 
     // first query row that sees a key of this block, and the query tiles from it
@@ -319,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         load_rows<D, NPW>(gg + (size_t)i0 * D, Nq - i0, stage + QTILE, w, voff);
         // 64 LSE and 64 D values (256 B each) land at lane*16 of a 1 KiB area;
         // lanes past 64 rows read zeros
-        const u32 nrec = (u32)min(max(Nq - i0, 0), CQ) * 4;
+        const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(Nq - i0, 0), CQ)) * 4;
         if (w == 0) lds_dma16(buffer_rsrc(lg + i0, nrec), stage + 2 * QTILE, (u32)lane * 16);
         if (w == 1) lds_dma16(buffer_rsrc(dg + i0, nrec), stage + 2 * QTILE + 1024, (u32)lane * 16);
     };
@@ -332,49 +425,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         dvacc[db] = f32x16{};
     }
 
-    // One query tile.  Causal: keys after a row's diagonal get P = 0 (also in
-    // tiles fully past the diagonal, where the test never fires).
-    auto step = [&](const unsigned char* st, int i0) {
+    // One query tile of two 32-row blocks.  The scores of the second block are
+    // issued before the first block's element-wise work, which then runs beside
+    // those matrix instructions.
+    auto step = [&](const unsigned char* st, int i0, auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
         const unsigned char* Qb = st;
         const unsigned char* Gb = st + QTILE;
         const float* Ls = (const float*)(st + 2 * QTILE);
         const float* Ds = (const float*)(st + 2 * QTILE + 1024);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                sacc = mfma32<BF16>(*(const u32x4*)(Qb + 32 * kb * ROWB + of.row[s]), kf[s], sacc);
-                pacc = mfma32<BF16>(*(const u32x4*)(Gb + 32 * kb * ROWB + of.row[s]), vf[s], pacc);
-            }
-            // register 8p + e stands for query row i0 + 32kb + 16p + 8h + e
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int rb = 32 * kb + 16 * p + 8 * h;
-                const f32x4 la = *(const f32x4*)(Ls + rb), lb = *(const f32x4*)(Ls + rb + 4);
-                const f32x4 da = *(const f32x4*)(Ds + rb), dbv = *(const f32x4*)(Ds + rb + 4);
-                const float lr[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
-                const float dr[8] = {da[0], da[1], da[2], da[3], dbv[0], dbv[1], dbv[2], dbv[3]};
-                float pr[8], ds[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pr[e] = exp2_fast(__builtin_fmaf(sacc[8 * p + e], a.c, -lr[e] * kLog2e));
-                    if (CAUSAL) pr[e] = (kj <= i0 + rb + e + off) ? pr[e] : 0.f;
-                    ds[e] = pr[e] * (pacc[8 * p + e] - dr[e]);
-                }
-                const u32x4 pb = {pack2<BF16>(pr[0], pr[1]), pack2<BF16>(pr[2], pr[3]),
-                                  pack2<BF16>(pr[4], pr[5]), pack2<BF16>(pr[6], pr[7])};
-                const u32x4 sb = {pack2<BF16>(ds[0], ds[1]), pack2<BF16>(ds[2], ds[3]),
-                                  pack2<BF16>(ds[4], ds[5]), pack2<BF16>(ds[6], ds[7])};
-                const unsigned char* qr = Qb + (32 * kb + 16 * p) * ROWB;
-                const unsigned char* gr = Gb + (32 * kb + 16 * p) * ROWB;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) {
-                    dvacc[db] = mfma32<BF16>(tr_operand<D>(gr, of, db), pb, dvacc[db]);
-                    dkacc[db] = mfma32<BF16>(tr_operand<D>(qr, of, db), sb, dkacc[db]);
-                }
-            }
-        }
+        const int lim = kj - i0 - off - 8 * h;
+        f32x16 s0, d0, s1, d1;
+        u32x4 pb[2], sb[2];
+        // scheduling fences keep the compiler to these four phases
+        scores<BF16, D>(Qb, Gb, 0, of, kf, vf, s0, d0);
+        __builtin_amdgcn_sched_barrier(0);
+        scores<BF16, D>(Qb, Gb, 1, of, kf, vf, s1, d1);
+        dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_accum<BF16, D>(Qb, Gb, 0, of, pb, sb, dkacc, dvacc);
+        u32x4 pb1[2], sb1[2];
+        dkdv_probs<BF16, MASK>(s1, d1, Ls, Ds, 32 + 8 * h, a.c, lim - 32, pb1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_accum<BF16, D>(Qb, Gb, 1, of, pb1, sb1, dkacc, dvacc);
     };
 
     // query tiles upward from the diagonal: the first ones may hold rows that do
@@ -387,8 +460,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const int tile = t0 + it;
         if (it + 1 < n_tiles) load_tile(tile + 1, nxt);
         const int i0 = tile * CQ;
-        // skip a wave whose keys no row of the tile sees yet
-        if (!CAUSAL || kw <= i0 + CQ - 1 + off) step(cur, i0);
+        // causal: a wave whose keys every row of the tile sees needs no mask, and
+        // one whose keys no row sees yet skips the tile
+        if (!CAUSAL || kw + 31 <= i0 + off) step(cur, i0, std::false_type{});
+        else if (kw <= i0 + CQ - 1 + off) step(cur, i0, std::true_type{});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
@@ -442,6 +517,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.dout = (const uint16_t*)p.dout;
     a.lse = p.lse;
     a.delta = p.delta;
+    a.lse2 = p.delta + (size_t)p.B * p.H * p.Nq;
     a.dq = (uint16_t*)p.dq;
     a.dk = (uint16_t*)p.dk;
     a.dv = (uint16_t*)p.dv;

@@ -159,7 +159,7 @@ fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o
                              fa_dtype dtype, void* stream);
 
 /*
- * Bytes of fp32 workspace fa_bwd needs: B * H * Nq * 4 (one value per query
+ * Bytes of fp32 workspace fa_bwd needs: B * H * Nq * 8 (two values per query
  * row).  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
@@ -171,9 +171,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
  * of being stored (Ringi, Lecture 25, section 3.3):
  *   dV = P^T dO;  dP = dO V^T;  dS = P o (dP - rowsum(dP o P));
  *   dQ = scale * dS K;  dK = scale * dS^T Q
- * rowsum(dP o P) equals rowsum(dO o O); the library computes it that way into
- * `workspace` (fp32, at least fa_bwd_workspace_bytes; its contents on entry do
- * not matter).  dK and dV are accumulated per key block over the query tiles and
+ * rowsum(dP o P) equals rowsum(dO o O); the library computes it that way,
+ * with lse rescaled to base 2, into `workspace` (fp32, at least
+ * fa_bwd_workspace_bytes; its contents on entry do not matter).  dK and dV are accumulated per key block over the query tiles and
  * dQ per query block over the key tiles, so no atomics are used and the results
  * are deterministic (LLM Infra Atlas, FA2 parallelism, section 5).  Same
  * conventions as fa_fwd (causal alignment, scale, rounding); lse and workspace

@@ -92,7 +92,7 @@ def bwd(q=A, k=A, v=A, o=A, g=A, lse=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 20, B=1
 
 
 def test_bwd_validation():
-    assert fa.bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+    assert fa.bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8
     assert fa.bwd_workspace_bytes(0, 3, 5) == 0
     assert bwd(g=NULL) == fa.FA_ERR_NULL
     assert bwd(ws=NULL) == fa.FA_ERR_NULL
