@@ -5,7 +5,9 @@ One step = one pass of the whole path over resident synthetic inputs:
     (B=1, H=32, Nq=Nk=8192, d=128, bf16, N(0,1)*0.5), and
   * decode: fa_fwd_splitkv + fa_splitkv_combine on the decode workload
     (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits), the same with the 32
-    query heads sharing 8 K/V heads (decode_gqa), and
+    query heads sharing 8 K/V heads (decode_gqa), and the same again with K/V in
+    a paged cache of 16-row pages scattered by a seeded permutation
+    (decode_paged), and
   * bwd: fa_bwd on the long-context causal workload (dO ~ N(0,1)), and
   * varlen: fa_fwd_varlen on 16 packed causal sequences (lengths log-uniform in
     [64, 8192], 20752 tokens) with 32 query heads sharing 8 K/V heads, d=128, bf16.
@@ -32,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_attention_22_amd import fa                          # noqa: E402
-from exact_attention_22_amd.inputs import BY_NAME, make_qkv, make_varlen     # noqa: E402
+from exact_attention_22_amd.inputs import BY_NAME, make_paged, make_qkv, make_varlen     # noqa: E402
 
 METRIC = "attn fwd TFLOPS & % MFMA peak (fp16 d=128 causal N=8K); decode HBM GB/s"
 PEAK_TFLOPS = {torch.bfloat16: 2500.0, torch.float16: 2500.0}   # MI355X dense MFMA
@@ -105,7 +107,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa", "bwd"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa", "decode_paged", "bwd"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=40000)
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -126,6 +128,8 @@ def main():
     do_v = args.only in ("all", "varlen")
     do_g = args.only in ("all", "decode_gqa")
     do_b = args.only in ("all", "bwd")
+    do_pg = args.only in ("all", "decode_paged")
+    wpg = BY_NAME["decode_paged"]
     if do_p:
         q, k, v = make_qkv(wp, device=dev)
         o = torch.empty_like(q)
@@ -161,6 +165,12 @@ def main():
         vo = torch.empty_like(vq)
         vlse = torch.empty((wv.H, vq.shape[0]), dtype=torch.float32, device=dev)
         vmax = max(wv.seqlens)
+    if do_pg:
+        pq, pkc, pvc, pbt, psl = make_paged(wpg, device=dev)
+        pop = torch.empty((wpg.splits, wpg.B, wpg.H, 1, wpg.d), dtype=torch.float32, device=dev)
+        plp = torch.empty((wpg.splits, wpg.B, wpg.H, 1), dtype=torch.float32, device=dev)
+        po = torch.empty((wpg.B, wpg.H, 1, wpg.d), dtype=wpg.dtype, device=dev)
+        plse = torch.empty((wpg.B, wpg.H, 1), dtype=torch.float32, device=dev)
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -173,7 +183,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e = [ev() for _ in range(8)]
+        e = [ev() for _ in range(10)]
         e[0].record(stream)
         if do_p:
             fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse, stream=stream)
@@ -200,6 +210,13 @@ def main():
             fa.bwd(q, k, v, bo, blse, bdo, causal=wp.causal, scale=wp.scale, dq=bdq, dk=bdk, dv=bdv, workspace=bws,
                    stream=stream)
         e[7].record(stream)
+        if do_pg:
+            fa.fwd_splitkv_paged(pq, pkc, pvc, pbt, psl, wpg.splits, scale=wpg.scale, o_part=pop, lse_part=plp,
+                                 stream=stream)
+        e[8].record(stream)
+        if do_pg:
+            fa.splitkv_combine(pop, plp, wpg.dtype, out=po, lse=plse, stream=stream)
+        e[9].record(stream)
         if rec is not None:
             rec.append(e)
 
@@ -219,6 +236,7 @@ def main():
     t_fwd, t_split, t_comb, t_var = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
     t_gsplit, t_gcomb = avg_ms(4, 5), avg_ms(5, 6)
     t_bwd = avg_ms(6, 7)
+    t_psplit, t_pcomb = avg_ms(7, 8), avg_ms(8, 9)
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic"}
@@ -302,6 +320,26 @@ def main():
         if not do_p and not do_d:
             out.update({"value": tf, "unit": "TFLOP/s", "dtype": "bf16"})
             cfg["workload"] = "varlen_gqa: 16 packed causal sequences, 20752 tokens, H=32 H_kv=8 d=128 bf16"
+    if do_pg:
+        # bytes the method must move: Q, O, K, V and LSE as decode_gqa, plus the
+        # block table (B x pages per sequence int32) once
+        kv = 2 * 2 * wpg.B * wpg.H_kv * wpg.Nk * wpg.d
+        pgb = 2 * 2 * wpg.B * wpg.H * wpg.d + kv + 4 * wpg.B * wpg.H + 4 * pbt.numel()
+        tp = t_psplit + t_pcomb
+        out["decode_paged"] = {"GB_per_s": pgb / (tp * 1e-3) / 1e9, "hbm_frac": pgb / (tp * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "us_total": tp * 1e3, "us_splitkv": t_psplit * 1e3, "us_combine": t_pcomb * 1e3,
+                               "algorithmic_bytes": pgb}
+        psplit_bytes = pgb - 2 * wpg.B * wpg.H * wpg.d - 4 * wpg.B * wpg.H
+        out["roofline_decode_paged"] = {"bound": "hbm", "achieved": psplit_bytes / (t_psplit * 1e-3) / 1e9,
+                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": psplit_bytes / (t_psplit * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                        "traffic": read_traffic("decode_paged", source_hash(DEC_SOURCES)),
+                                        "kernel": "decode_kernel<fp16, d=128, 4 query heads per workgroup, paged>"}
+        cfg["decode_paged"] = {"B": wpg.B, "H": wpg.H, "H_kv": wpg.H_kv, "Nq": 1, "Nk": wpg.Nk, "d": wpg.d,
+                               "dtype": "fp16", "splits": wpg.splits, "page_size": wpg.page_size}
+        if args.only == "decode_paged":
+            out.update({"value": out["decode_paged"]["GB_per_s"], "unit": "GB/s", "dtype": "f16"})
+            cfg["workload"] = "decode_paged: B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 fp16 16 splits, 16-row pages"
     out["config"] = cfg
     if do_p and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(q, k, v, wp, args.cpu_rows)

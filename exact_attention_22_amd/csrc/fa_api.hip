@@ -157,6 +157,36 @@ fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, float*
                         stream);
 }
 
+fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seqlens_k,
+                               float* o_part, float* lse_part,
+                               int B, int H, int H_kv, int d, int page_size, int max_pages, int num_pages,
+                               float scale, int num_splits, fa_dtype dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !o_part || !lse_part) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || num_splits < 1) return FA_ERR_SHAPE;
+    if (page_size < 1 || (page_size & (page_size - 1)) != 0) return FA_ERR_SHAPE;
+    if (max_pages < 1 || num_pages < 1 || (int64_t)max_pages * page_size > INT32_MAX) return FA_ERR_SHAPE;
+    if (count4(num_pages, page_size, H_kv, d) < 0 || count4(B, H, d, num_splits) < 0 ||
+        count4(B, max_pages, 1, 1) < 0)
+        return FA_ERR_SHAPE;
+    if ((int64_t)B * H > INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) ||
+        ((uintptr_t)lse_part & 3u) || ((uintptr_t)block_table & 3u) || ((uintptr_t)seqlens_k & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k_cache, v_cache, o_part, lse_part, B, H, 1, max_pages * page_size, d, false,
+                    dtype == FA_BF16, scale, num_splits};
+    p.H_kv = H_kv;
+    p.block_table = block_table;
+    p.seqlens_k = seqlens_k;
+    p.page_size = page_size;
+    p.max_pages = max_pages;
+    p.num_pages = num_pages;
+    return from_hip(fa::launch_decode(p, (hipStream_t)stream));
+}
+
 fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                              int B, int H, int Nq, int d, int num_splits, fa_dtype dtype, void* stream) {
     if (!o_part || !lse_part || !o || !lse) return FA_ERR_NULL;

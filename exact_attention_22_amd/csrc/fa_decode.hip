@@ -21,6 +21,16 @@
 // heads of one workgroup read the same K/V head, so the workgroup streams that
 // head's chunk once and scores every loaded key row against all GP queries;
 // decode bytes per query head fall by GP.
+//
+// Paged K/V cache (the pages pose it: a cache scattered over fixed-size pages
+// and how the load addressing changes; KingOfEgg, "Flash Attention (4)",
+// question on PagedAttention): keys live in pages of page_size rows
+// [num_pages, page_size, H_kv, d]; sequence b's logical page j sits in the
+// physical page block_table[b][j].  A key row stays 256 contiguous bytes (d =
+// 128), so every wavefront load still reads whole rows; each lane resolves its
+// own key's page, and the page entries of the next step are fetched one step
+// ahead so the indirection adds no latency.  Each sequence has its own length
+// and is split into num_splits equal chunks.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -37,6 +47,11 @@ struct DecArgs {
     int split_chunk;
     float c;   // scale * log2(e), sign included
     int H, H_kv, group;   // query heads, K/V heads, query heads per K/V head
+    // paged K/V cache
+    const int* block_table;   // [B, max_pages]
+    const int* seqlens;       // [B]
+    int page_shift;           // log2(page_size)
+    int max_pages, num_pages;
 };
 
 template <int CTRL>
@@ -67,8 +82,9 @@ __device__ __forceinline__ void widen8(u32x4 x, float* f) {
     }
 }
 
-// GP: query heads per workgroup (a divisor of the group size).
-template <bool BF16, int D, int GP>
+// GP: query heads per workgroup (a divisor of the group size).  PAGED: k and v
+// are the paged caches.
+template <bool BF16, int D, int GP, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     constexpr int CH = D / 8;          // lanes per key row
     constexpr int KPI = 64 / CH;       // key rows per wavefront load
@@ -83,12 +99,33 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = lane % CH, r = lane / CH;
 
-    const int ks = min(a.Nk, split * a.split_chunk);
-    const int ke = min(a.Nk, ks + a.split_chunk);
+    int ks, ke;
+    const uint16_t* kg;
+    const uint16_t* vg;
+    const int* bt = nullptr;   // this sequence's row of the block table
+    int hk = 0;
+    if constexpr (PAGED) {
+        const int b = bh0 / a.H;
+        hk = (bh0 % a.H) / a.group;
+        const int len = a.seqlens[b];
+        // a length outside [0, max_pages * page_size] leaves the rows unwritten
+        if (len < 0 || len > (a.max_pages << a.page_shift)) return;
+        const int chunk = (len + a.S - 1) / a.S;
+        ks = min(len, split * chunk);
+        ke = min(len, ks + chunk);
+        kg = a.k;
+        vg = a.v;
+        bt = a.block_table + (size_t)b * a.max_pages;
+    } else {
+        ks = min(a.Nk, split * a.split_chunk);
+        ke = min(a.Nk, ks + a.split_chunk);
+        kg = a.k + (size_t)bkv * a.Nk * D;
+        vg = a.v + (size_t)bkv * a.Nk * D;
+    }
     const int ngroups = (ke - ks + KPI - 1) / KPI;
-
-    const uint16_t* kg = a.k + (size_t)bkv * a.Nk * D;
-    const uint16_t* vg = a.v + (size_t)bkv * a.Nk * D;
+    // physical page of a key of this split (-1 past the split's end); only keys
+    // below the sequence length index the block table
+    auto page_of = [&](int key) -> int { return key < ke ? bt[key >> a.page_shift] : -1; };
 
     float qv[GP][8];
 #pragma unroll
@@ -107,19 +144,39 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
     }
 
+    // page entries of the first step (paged)
+    int pnext[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) pnext[u] = PAGED ? page_of(ks + (w + 4 * u) * KPI + r) : 0;
+
     for (int g0 = w; g0 < ngroups; g0 += 4 * U) {
         u32x4 kr[U], vr[U];
         int key[U];
+        bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             key[u] = ks + (g0 + 4 * u) * KPI + r;
-            if (key[u] < ke) {
-                kr[u] = *(const u32x4*)(kg + (size_t)key[u] * D + 8 * c);
-                vr[u] = *(const u32x4*)(vg + (size_t)key[u] * D + 8 * c);
+            size_t row;
+            if constexpr (PAGED) {
+                // a page entry outside [0, num_pages) drops its keys
+                const int pg = pnext[u];
+                ok[u] = key[u] < ke && (unsigned)pg < (unsigned)a.num_pages;
+                row = (((size_t)pg << a.page_shift) + (key[u] & ((1 << a.page_shift) - 1))) * a.H_kv + hk;
+            } else {
+                ok[u] = key[u] < ke;
+                row = (size_t)key[u];
+            }
+            if (ok[u]) {
+                kr[u] = *(const u32x4*)(kg + row * D + 8 * c);
+                vr[u] = *(const u32x4*)(vg + row * D + 8 * c);
             } else {
                 kr[u] = u32x4{0, 0, 0, 0};
                 vr[u] = u32x4{0, 0, 0, 0};
             }
+        }
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) pnext[u] = page_of(key[u] + 4 * U * KPI);   // next step's keys
         }
         float s[GP][U];
         float mx[GP];
@@ -135,7 +192,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qv[g][i], kf[i], part);
                 s[g][u] = row_sum<CH>(part);
-                if (key[u] >= ke) s[g][u] = -INFINITY;
+                if (!ok[u]) s[g][u] = -INFINITY;
                 mx[g] = fmaxf(mx[g], s[g][u]);
             }
         }
@@ -225,15 +282,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (lane == 0) lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool PAGED>
 hipError_t launch_dec(const DecArgs& a, int gp, int blocks, hipStream_t stream) {
     switch (gp) {
-        case 8: hipLaunchKernelGGL((decode_kernel<BF16, D, 8>), dim3(blocks), dim3(256), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4>), dim3(blocks), dim3(256), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2>), dim3(blocks), dim3(256), 0, stream, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<BF16, D, 1>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_kernel<BF16, D, 8, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<BF16, D, 1, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
     }
     return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_dec_d(const DecArgs& a, int d, bool bf16, int gp, int blocks, hipStream_t stream) {
+    if (d == 128) return bf16 ? launch_dec<true, 128, PAGED>(a, gp, blocks, stream)
+                              : launch_dec<false, 128, PAGED>(a, gp, blocks, stream);
+    return bf16 ? launch_dec<true, 64, PAGED>(a, gp, blocks, stream) : launch_dec<false, 64, PAGED>(a, gp, blocks, stream);
 }
 
 }  // namespace
@@ -257,9 +321,14 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
     const int gp = a.group % 8 == 0 ? 8 : a.group % 4 == 0 ? 4 : a.group % 2 == 0 ? 2 : 1;
     const int64_t blocks = (int64_t)a.BH / gp * a.S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (p.d == 128) return p.bf16 ? launch_dec<true, 128>(a, gp, (int)blocks, stream)
-                                  : launch_dec<false, 128>(a, gp, (int)blocks, stream);
-    return p.bf16 ? launch_dec<true, 64>(a, gp, (int)blocks, stream) : launch_dec<false, 64>(a, gp, (int)blocks, stream);
+    a.block_table = p.block_table;
+    a.seqlens = p.seqlens_k;
+    a.max_pages = p.max_pages;
+    a.num_pages = p.num_pages;
+    a.page_shift = 0;
+    while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
+    if (p.block_table) return launch_dec_d<true>(a, p.d, p.bf16, gp, (int)blocks, stream);
+    return launch_dec_d<false>(a, p.d, p.bf16, gp, (int)blocks, stream);
 }
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,

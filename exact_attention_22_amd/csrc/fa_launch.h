@@ -26,6 +26,11 @@ struct FwdParams {
     const int* cu_k;
     int H_kv;
     int total_q, total_k;
+    // paged K/V cache for the single-row decode (k, v: [num_pages, page_size,
+    // H_kv, d]; Nk unused): non-null block_table selects it
+    const int* block_table = nullptr;   // device, [B, max_pages]
+    const int* seqlens_k = nullptr;     // device, [B]
+    int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 // Validated arguments of one backward launch ([B, H, N, d] tensors; delta is

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
-           "fa_fwd_splitkv_gqa", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str")
+           "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -48,6 +49,8 @@ def lib():
         L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_fwd_splitkv.restype = i
         L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.fa_fwd_splitkv_paged.restype = i
+        L.fa_fwd_splitkv_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
         L.fa_splitkv_combine.restype = i
         L.fa_splitkv_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -208,6 +211,50 @@ def fwd_splitkv_gqa(q, k, v, num_splits, causal=False, scale=None, o_part=None, 
     _check(lib().fa_fwd_splitkv_gqa(qp, kp, vp, opp, lpp, B, H, H_kv, Nq, Nk, d, int(bool(causal)),
                                     _scale(scale, d), S, _DTYPES[q.dtype], _stream(stream)))
     return o_part, lse_part
+
+
+def fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits, scale=None, o_part=None,
+                      lse_part=None, stream=None):
+    """Split-KV partials of one query row per sequence over a paged K/V cache.
+
+    q [B, H, d]; k_cache, v_cache [num_pages, page_size, H_kv, d]; block_table
+    int32 [B, max_pages] and seqlens_k int32 [B] on the device.  Returns o_part
+    [S, B, H, 1, d] and lse_part [S, B, H, 1] (fp32) for splitkv_combine.
+    """
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, H, d] and the caches [num_pages, page_size, H_kv, d]")
+    B, H, d = q.shape
+    num_pages, page_size, H_kv = k_cache.shape[:3]
+    if tuple(k_cache.shape) != (num_pages, page_size, H_kv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H_kv, d] with q's d")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seqlens_k.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seqlens_k [B]")
+    max_pages = block_table.shape[1]
+    qp, kp, vp = (_dev_tensor(t, n, q.dtype) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")))
+    btp = _dev_tensor(block_table, "block_table", torch.int32)
+    slp = _dev_tensor(seqlens_k, "seqlens_k", torch.int32)
+    S = int(num_splits)
+    if o_part is None:
+        o_part = torch.empty((S, B, H, 1, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((S, B, H, 1), dtype=torch.float32, device=q.device)
+    if tuple(o_part.shape) != (S, B, H, 1, d) or tuple(lse_part.shape) != (S, B, H, 1):
+        raise ValueError("o_part must be [S, B, H, 1, d] and lse_part [S, B, H, 1]")
+    opp = _dev_tensor(o_part, "o_part", torch.float32)
+    lpp = _dev_tensor(lse_part, "lse_part", torch.float32)
+    _check(lib().fa_fwd_splitkv_paged(qp, kp, vp, btp, slp, opp, lpp, B, H, H_kv, d, page_size, max_pages,
+                                      num_pages, _scale(scale, d), S, _DTYPES[q.dtype], _stream(stream)))
+    return o_part, lse_part
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits=16, scale=None, stream=None,
+                 o_part=None, lse_part=None):
+    """fwd_splitkv_paged followed by the combine: O [B, H, 1, d], LSE [B, H, 1]."""
+    o_part, lse_part = fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits, scale,
+                                         o_part, lse_part, stream)
+    return splitkv_combine(o_part, lse_part, q.dtype, stream=stream)
 
 
 def splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, stream=None):

@@ -15,6 +15,9 @@ Workloads (Q, K, V iid N(0, 1), layout [B, H, N, d], scale = 1/sqrt(d)):
   varlen_gqa      16 packed sequences, lengths log-uniform in [64, 8192] (seeded),
                   H=32 query heads sharing H_kv=8 K/V heads, d=128 bf16 causal,
                   Nq = Nk per sequence; layout [total, heads, d]
+  decode_paged    as decode_gqa with K/V in a paged cache of 16-row pages
+                  [num_pages, 16, H_kv, d], pages assigned by a seeded
+                  permutation (a fragmented cache); q [B, H, d]
 These follow the shapes the pages benchmark (randn fp16, d in {64, 128},
 N from 1K to 16K) -- no dataset is involved.
 """
@@ -42,6 +45,7 @@ class Workload:
     seed: int = 42
     H_kv: int = 0            # K/V heads when grouped (0: H)
     seqlens: tuple = ()      # non-empty: packed layout with these lengths (queries = keys)
+    page_size: int = 0       # > 0: decode from a paged K/V cache with pages of this many rows
 
     @property
     def scale(self) -> float:
@@ -67,6 +71,7 @@ WORKLOADS = [
     Workload("long_causal", 1, 32, 8192, 8192, 128, BF16, True, mult=0.5, seed=45),
     Workload("decode", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=46),
     Workload("decode_gqa", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=48, H_kv=8),
+    Workload("decode_paged", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=49, H_kv=8, page_size=16),
     Workload("varlen_gqa", len(_VARLEN_LENS), 32, max(_VARLEN_LENS), max(_VARLEN_LENS), 128, BF16, True,
              seed=47, H_kv=8, seqlens=_VARLEN_LENS),
 ]
@@ -135,3 +140,54 @@ def make_partials(S, B, H, Nq, d, seed=7, device="cpu", empty_every=0):
         empty = ((s_idx + r_idx) % empty_every == 0).reshape(S, B, H, Nq)
         lse[empty] = -math.inf
     return o, lse
+
+
+def make_paged(w: Workload, device="cpu", seqlens=None, spare_pages=0, fill=float("nan")):
+    """A paged K/V cache for a single-row decode workload.
+
+    Returns q [B, H, d]; k_cache, v_cache [num_pages, page_size, H_kv, d] holding
+    key t of sequence b at row t % page_size of page block_table[b][t //
+    page_size]; block_table int32 [B, max_pages] (-1 past a sequence's pages);
+    seqlens int32 [B] (default Nk for every sequence).  Q, then every sequence's
+    K and V (token-major) are drawn as in make_qkv; physical pages are handed out
+    in the order of a seeded permutation, so consecutive logical pages are
+    scattered.  Rows past a sequence's end and `spare_pages` unused pages hold
+    `fill` (NaN by default: a kernel that reads them produces NaN).
+    """
+    lens = [int(n) for n in (seqlens if seqlens is not None else [w.Nk] * w.B)]
+    B, ps, hk = len(lens), w.page_size, w.H_kv or w.H
+    npg = [-(-n // ps) for n in lens]
+    max_pages = max(1, max(npg))
+    num_pages = max(1, sum(npg) + spare_pages)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    total = sum(lens)
+    drawn = []
+    for shape in ((B, w.H, w.d), (total, hk, w.d), (total, hk, w.d)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+        if w.mult != 1.0:
+            x.mul_(w.mult)
+        drawn.append(x.to(w.dtype))
+        del x
+    q, k_tok, v_tok = drawn
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(w.seed + 1000))
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    page_of_tok, row_of_tok = [], []
+    nxt = 0
+    for b, n in enumerate(lens):
+        pages = perm[nxt:nxt + npg[b]]
+        nxt += npg[b]
+        table[b, :npg[b]] = pages.to(torch.int32)
+        t = torch.arange(n)
+        page_of_tok.append(pages[t // ps])
+        row_of_tok.append(t % ps)
+    caches = []
+    for tok in (k_tok, v_tok):
+        cache = torch.full((num_pages, ps, hk, w.d), fill, dtype=w.dtype, device=device)
+        if total:
+            pi = torch.cat(page_of_tok).to(device)
+            ri = torch.cat(row_of_tok).to(device)
+            cache[pi, ri] = tok
+        caches.append(cache)
+    del k_tok, v_tok
+    return q, caches[0], caches[1], table.to(device), torch.tensor(lens, dtype=torch.int32, device=device)

@@ -147,6 +147,36 @@ fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v,
                              int num_splits, fa_dtype dtype, void* stream);
 
 /*
+ * Split-KV decode over a paged K/V cache: one query row per sequence and head
+ * (q [B, H, d]) attending to that sequence's cached keys, which are scattered
+ * over fixed-size pages (KingOfEgg, "Flash Attention (4)", the PagedAttention
+ * question: a K/V cache split into non-contiguous pages, the kernel's address
+ * computation going through a page table).
+ *   k_cache, v_cache  [num_pages, page_size, H_kv, d]  dtype, 16-byte aligned
+ *   block_table       [B, max_pages]  int32, device: physical page of logical
+ *                     page j of sequence b (key t lives at row t % page_size of
+ *                     page block_table[b][t / page_size])
+ *   seqlens_k         [B]  int32, device: cached keys of sequence b
+ * Query head h reads K/V head h / (H / H_kv).  Sequence b is split into
+ * num_splits chunks of c_b = ceil(seqlens_k[b] / num_splits) keys; split s
+ * covers keys [s*c_b, min(len_b, (s+1)*c_b)).  The outputs are the partials of
+ * fa_fwd_splitkv with Nq = 1 (o_part [num_splits, B, H, 1, d], lse_part
+ * [num_splits, B, H, 1], sized by fa_splitkv_workspace_bytes(B, H, 1, d,
+ * num_splits)), merged by fa_splitkv_combine.  A sequence of length 0 gives
+ * O = 0 and LSE = -inf.  Requirements: page_size a power of two, H % H_kv == 0,
+ * num_splits >= 1, max_pages * page_size <= INT32_MAX; block_table and
+ * seqlens_k 4-byte aligned.  The table and lengths live on the device and are
+ * not read by the host: a length outside [0, max_pages * page_size] leaves that
+ * sequence's partials unwritten, and a page entry outside [0, num_pages) drops
+ * its keys; no memory outside the tensors is accessed.
+ */
+fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seqlens_k,
+                               float* o_part, float* lse_part,
+                               int B, int H, int H_kv, int d, int page_size, int max_pages, int num_pages,
+                               float scale, int num_splits, fa_dtype dtype, void* stream);
+
+/*
  * Split-KV forward, second half: merge the partials with the online-softmax
  * identity (Ringi, Lecture 25, section 2.2).  Per row:
  *   M = max_s lse_part[s];  w_s = exp(lse_part[s] - M) (0 for -inf);

@@ -208,6 +208,64 @@ class Oracle:
             return o.reshape(total_q, H, d), lse.reshape(total_q, H).T.copy()
         return o, lse
 
+    # -- paged K/V cache ---------------------------------------------------
+    @staticmethod
+    def gather_pages(cache, block_table, seqlens):
+        """The keys of a paged cache in sequence order, token-major: for sequence
+        b and t = 0 .. len_b - 1, row t % page_size of physical page
+        block_table[b][t // page_size] (the page-table indirection the pages pose
+        for a cache split into non-contiguous pages: KingOfEgg, "Flash Attention
+        (4)", PagedAttention question).  cache [num_pages, page_size, H_kv, d]
+        -> [sum(len_b), H_kv, d]."""
+        page_size = cache.shape[1]
+        table = np.asarray(block_table, dtype=np.int64)
+        rows = []
+        for b in range(table.shape[0]):
+            for t in range(int(seqlens[b])):
+                rows.append(cache[int(table[b, t // page_size]), t % page_size])
+        if not rows:
+            return cache.new_empty((0,) + tuple(cache.shape[2:]))
+        return torch.stack(rows).contiguous()
+
+    def attention_paged(self, q, k_cache, v_cache, block_table, seqlens, scale, nthreads=None):
+        """fp64 single-row decode over a paged cache: q [B, H, d] (one query row
+        per sequence and head) against the len_b keys of sequence b gathered
+        through its block table; query head h reads K/V head h // (H // H_kv).
+        Returns o [B, H, d] and lse [B, H] (o = 0, lse = -inf for an empty
+        sequence)."""
+        B, H, d = q.shape
+        lens = [int(n) for n in seqlens]
+        k = self.gather_pages(k_cache, block_table, lens)
+        v = self.gather_pages(v_cache, block_table, lens)
+        if k.shape[0] == 0:
+            return np.zeros((B, H, d)), np.full((B, H), -np.inf)
+        cu_q = np.arange(B + 1, dtype=np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        o, lse = self.attention_varlen(q.contiguous(), k, v, cu_q, cu_k, False, scale, nthreads=nthreads)
+        return o, lse.T.copy()
+
+    def split_partials_paged(self, q, k_cache, v_cache, block_table, seqlens, scale, num_splits,
+                             nthreads=None):
+        """Per-split normalised partials of attention_paged: sequence b's keys are
+        cut into num_splits chunks of ceil(len_b / num_splits) keys (the split rule
+        of split_ranges applied per sequence).  Returns o_part [S, B, H, 1, d] and
+        lse_part [S, B, H, 1]."""
+        B, H, d = q.shape
+        S = num_splits
+        o_part = np.zeros((S, B, H, 1, d))
+        lse_part = np.full((S, B, H, 1), -np.inf)
+        for b in range(B):
+            n = int(seqlens[b])
+            if n == 0:
+                continue
+            kb = self.gather_pages(k_cache, block_table[b:b + 1], [n]).permute(1, 0, 2).unsqueeze(0).contiguous()
+            vb = self.gather_pages(v_cache, block_table[b:b + 1], [n]).permute(1, 0, 2).unsqueeze(0).contiguous()
+            ob, lb = self.split_partials(q[b:b + 1, :, None, :].contiguous(), kb, vb, False, scale, S,
+                                         nthreads=nthreads)
+            o_part[:, b] = ob[:, 0]
+            lse_part[:, b] = lb[:, 0]
+        return o_part, lse_part
+
     # -- split-KV ---------------------------------------------------------
     @staticmethod
     def split_ranges(Nk, num_splits):

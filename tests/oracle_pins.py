@@ -11,7 +11,8 @@ Sources for the facts used here:
   explained", section 5.1 (causal mask, -inf before softmax) and its forward
   pseudocode (L = m + log l);  LLM Infra Atlas "FA2: parallelism", section 4
   (causal bound offset by seqlen_k - seqlen_q);  KingOfEgg "Flash Attention (4)",
-  section 3.5 (empty row: inv_sum = 1 so O = 0).
+  section 3.5 (empty row: inv_sum = 1 so O = 0), and its PagedAttention question
+  (a K/V cache in non-contiguous pages reached through a page table).
 """
 import json
 import math
@@ -496,9 +497,120 @@ def pin_bwd_rows(orc):
     _close(sv, dv.reshape(-1, d)[kr], 0.0, "bwd selected dV rows")
 
 
+# -- paged K/V cache (KingOfEgg, "Flash Attention (4)", PagedAttention question) --
+def _paged_from_contiguous(k, lens, page_size, order):
+    """Pin-side paging of contiguous k [B, H_kv, N, d]: sequence b's logical page j
+    goes to physical page order[next free]; returns the cache [P, page_size,
+    H_kv, d] (unused rows zero) and the block table."""
+    B, H_kv, N, d = k.shape
+    npg = [-(-n // page_size) for n in lens]
+    P = sum(npg)
+    cache = torch.zeros((P, page_size, H_kv, d), dtype=k.dtype)
+    table = np.full((B, max(1, max(npg))), -1, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        for j in range(npg[b]):
+            phys = order[nxt]
+            nxt += 1
+            table[b, j] = phys
+            for r in range(page_size):
+                t = j * page_size + r
+                if t < lens[b]:
+                    cache[phys, r] = k[b, :, t]
+    return cache, table
+
+
+def pin_paged_matches_contiguous(orc):
+    """Decode over a shuffled paged cache equals decode over the same keys laid
+    out contiguously (per sequence, grouped heads)."""
+    B, H, H_kv, N, d, ps = 3, 4, 2, 23, 16, 4
+    lens = [23, 9, 1]
+    for dt in DTYPES:
+        q = _rand((B, H, d), dt, 501)
+        k = _rand((B, H_kv, N, d), dt, 502)
+        v = _rand((B, H_kv, N, d), dt, 503)
+        P = sum(-(-n // ps) for n in lens)
+        order = list(np.random.default_rng(504).permutation(P))
+        kc, table = _paged_from_contiguous(k, lens, ps, order)
+        vc, _ = _paged_from_contiguous(v, lens, ps, order)
+        o, lse = orc.attention_paged(q, kc, vc, table, lens, 0.3, nthreads=2)
+        for b in range(B):
+            n = lens[b]
+            ro, rl = orc.attention_gqa(q[b:b + 1, :, None, :].contiguous(), k[b:b + 1, :, :n].contiguous(),
+                                       v[b:b + 1, :, :n].contiguous(), False, 0.3, nthreads=1)
+            _close(o[b], ro.reshape(H, d), 1e-12, f"paged O, sequence {b}, {dt}")
+            _close(lse[b], rl.reshape(H), 1e-12, f"paged LSE, sequence {b}, {dt}")
+
+
+def pin_paged_brute_force(orc):
+    """A tiny paged decode computed by hand: page lookup, dot products and a
+    softmax with math.exp, in Python floats."""
+    ps, d, H, H_kv = 2, 3, 2, 1
+    lens = [3, 4]
+    # values on a 1/4 grid are exact in fp16 and bf16
+    kc = _rand((5, ps, H_kv, d), torch.float16, 511, -2, 2, 0.25)
+    vc = _rand((5, ps, H_kv, d), torch.float16, 512, -2, 2, 0.25)
+    q = _rand((2, H, d), torch.float16, 513, -2, 2, 0.25)
+    table = np.array([[4, 1], [0, 3]], dtype=np.int32)
+    scale = 0.625   # exact in float32, the type the oracle receives
+    o, lse = orc.attention_paged(q, kc, vc, table, lens, scale, nthreads=1)
+    for b in range(2):
+        for h in range(H):
+            keys, vals = [], []
+            for t in range(lens[b]):
+                page, row = int(table[b][t // ps]), t % ps
+                keys.append([float(x) for x in kc[page, row, 0]])
+                vals.append([float(x) for x in vc[page, row, 0]])
+            qq = [float(x) for x in q[b, h]]
+            sc = [scale * sum(a * c for a, c in zip(qq, kk)) for kk in keys]
+            m = max(sc)
+            w = [math.exp(x - m) for x in sc]
+            l = sum(w)
+            exp_o = [sum(wi * vv[t] for wi, vv in zip(w, vals)) / l for t in range(d)]
+            _close(o[b, h], exp_o, 1e-12, f"paged brute-force O ({b}, {h})")
+            _close(lse[b, h], m + math.log(l), 1e-12, f"paged brute-force LSE ({b}, {h})")
+
+
+def pin_paged_empty_sequence(orc):
+    """A sequence with no cached keys gives O = 0 and LSE = -inf; the others are
+    unaffected."""
+    q = _rand((2, 2, 8), torch.bfloat16, 521)
+    kc = _rand((2, 4, 1, 8), torch.bfloat16, 522)
+    vc = _rand((2, 4, 1, 8), torch.bfloat16, 523)
+    table = np.array([[0, 1], [-1, -1]], dtype=np.int32)
+    o, lse = orc.attention_paged(q, kc, vc, table, [6, 0], 0.5, nthreads=1)
+    _close(o[1], np.zeros((2, 8)), 0.0, "paged empty sequence O")
+    assert np.all(np.isneginf(lse[1])), "paged empty sequence LSE must be -inf"
+    o1, l1 = orc.attention_paged(q[:1].contiguous(), kc, vc, table[:1], [6], 0.5, nthreads=1)
+    _close(o[0], o1[0], 0.0, "paged O unaffected by an empty neighbour")
+    _close(lse[0], l1[0], 0.0, "paged LSE unaffected by an empty neighbour")
+
+
+def pin_paged_splits(orc):
+    """Paged partials split each sequence into chunks of ceil(len / S) keys
+    (10 keys, S = 4: [0,3) [3,6) [6,9) [9,10)); they merge back to the whole."""
+    B, H, H_kv, d, ps = 1, 2, 1, 8, 4
+    n, S = 10, 4
+    q = _rand((B, H, d), torch.float16, 531)
+    k = _rand((B, H_kv, n, d), torch.float16, 532)
+    v = _rand((B, H_kv, n, d), torch.float16, 533)
+    kc, table = _paged_from_contiguous(k, [n], ps, [2, 0, 1])
+    vc, _ = _paged_from_contiguous(v, [n], ps, [2, 0, 1])
+    op, lp = orc.split_partials_paged(q, kc, vc, table, [n], 0.4, S, nthreads=1)
+    for s, kr in enumerate([(0, 3), (3, 6), (6, 9), (9, 10)]):
+        ro, rl = orc.attention_gqa(q[:, :, None, :].contiguous(), k, v, False, 0.4, key_range=kr, nthreads=1)
+        _close(op[s], ro, 1e-12, f"paged split {s} O")
+        _close(lp[s], rl, 1e-12, f"paged split {s} LSE")
+    oc, lc = orc.combine(op, lp)
+    o, lse = orc.attention_paged(q, kc, vc, table, [n], 0.4, nthreads=1)
+    _close(oc.reshape(H, d), o[0], 1e-12, "paged combined O")
+    _close(lc.reshape(H), lse[0], 1e-12, "paged combined LSE")
+
+
 ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
             pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows,
             pin_dense_grouped_heads, pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_scale_zero,
-            pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows]
+            pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows, pin_paged_matches_contiguous,
+            pin_paged_brute_force, pin_paged_empty_sequence, pin_paged_splits]

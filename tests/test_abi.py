@@ -146,6 +146,34 @@ def combine(op=A, lp=A, o=A, lse=A, B=1, H=1, Nq=1, d=64, S=4, dtype=0):
     return fa.lib().fa_splitkv_combine(op, lp, o, lse, B, H, Nq, d, S, dtype, NULL)
 
 
+def paged(q=A, kc=A, vc=A, bt=A, sl=A, op=A, lp=A, B=2, H=4, H_kv=2, d=128, ps=16, max_pages=8, num_pages=16,
+          scale=0.1, S=4, dtype=0):
+    return fa.lib().fa_fwd_splitkv_paged(q, kc, vc, bt, sl, op, lp, B, H, H_kv, d, ps, max_pages, num_pages,
+                                         scale, S, dtype, NULL)
+
+
+def test_paged_validation():
+    for kw in ("q", "kc", "vc", "bt", "sl", "op", "lp"):
+        assert paged(**{kw: NULL}) == fa.FA_ERR_NULL, kw
+    assert paged(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert paged(dtype=5) == fa.FA_ERR_UNSUPPORTED
+    assert paged(scale=float("inf")) == fa.FA_ERR_UNSUPPORTED
+    assert paged(H=6, H_kv=4) == fa.FA_ERR_SHAPE
+    assert paged(H_kv=0) == fa.FA_ERR_SHAPE
+    assert paged(B=0) == fa.FA_ERR_SHAPE
+    assert paged(S=0) == fa.FA_ERR_SHAPE
+    assert paged(ps=12) == fa.FA_ERR_SHAPE          # not a power of two
+    assert paged(ps=0) == fa.FA_ERR_SHAPE
+    assert paged(max_pages=0) == fa.FA_ERR_SHAPE
+    assert paged(num_pages=0) == fa.FA_ERR_SHAPE
+    assert paged(max_pages=1 << 28, ps=16) == fa.FA_ERR_SHAPE   # logical keys past int32
+    assert paged(q=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert paged(kc=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert paged(op=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert paged(bt=ctypes.c_void_p(0x10002)) == fa.FA_ERR_UNSUPPORTED
+    assert paged(sl=ctypes.c_void_p(0x10001)) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_combine_validation():
     assert combine(lp=NULL) == fa.FA_ERR_NULL
     assert combine(S=0) == fa.FA_ERR_SHAPE

@@ -4,6 +4,9 @@ the oracle -- the scores, the mask, the softmax, the LSE, the decoders and the
 split merge."""
 import os
 
+import numpy as np
+import torch
+
 import pytest
 
 from oracle import build, oracle
@@ -83,3 +86,36 @@ def test_dense_grouped_heads_mapping_mutant_is_caught():
 
     with pytest.raises(AssertionError):
         oracle_pins.pin_dense_grouped_heads(Tiled())
+
+
+@pytest.mark.parametrize("kind", ["row_page_swapped", "first_table_row", "page_off_by_one"])
+def test_paged_gather_mutants_are_caught(kind):
+    """Plausible mistakes in the page-table gather fail the paged pins."""
+    class Broken(oracle.Oracle):
+        @staticmethod
+        def gather_pages(cache, block_table, seqlens):
+            ps = cache.shape[1]
+            table = np.asarray(block_table, dtype=np.int64)
+            rows = []
+            for b in range(table.shape[0]):
+                for t in range(int(seqlens[b])):
+                    if kind == "row_page_swapped":
+                        page, row = int(table[b, t % table.shape[1]]), (t // table.shape[1]) % ps
+                    elif kind == "first_table_row":
+                        page, row = int(table[0, t // ps]), t % ps
+                    else:
+                        page, row = int(table[b, t // ps]), (t + 1) % ps
+                    rows.append(cache[page, row])
+            if not rows:
+                return cache.new_empty((0,) + tuple(cache.shape[2:]))
+            return torch.stack(rows).contiguous()
+
+    orc = Broken()
+    caught = 0
+    for pin in (oracle_pins.pin_paged_matches_contiguous, oracle_pins.pin_paged_brute_force,
+                oracle_pins.pin_paged_splits):
+        try:
+            pin(orc)
+        except (AssertionError, IndexError, RuntimeError):
+            caught += 1
+    assert caught, f"no paged pin catches the {kind} mutant"
