@@ -23,7 +23,7 @@
 // decode bytes per query head fall by GP.
 //
 // Paged K/V cache (the pages pose it: a cache scattered over fixed-size pages
-// and how the load addressing changes; KingOfEgg, "Flash Attention (4)",
+// and how the load addressing changes; Ringi, "Lecture 25", section 8.3,
 // question on PagedAttention): keys live in pages of page_size rows
 // [num_pages, page_size, H_kv, d]; sequence b's logical page j sits in the
 // physical page block_table[b][j].  A key row stays 256 contiguous bytes (d =

@@ -149,7 +149,7 @@ fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v,
 /*
  * Split-KV decode over a paged K/V cache: one query row per sequence and head
  * (q [B, H, d]) attending to that sequence's cached keys, which are scattered
- * over fixed-size pages (KingOfEgg, "Flash Attention (4)", the PagedAttention
+ * over fixed-size pages (Ringi, "Lecture 25", section 8.3, the PagedAttention
  * question: a K/V cache split into non-contiguous pages, the kernel's address
  * computation going through a page table).
  *   k_cache, v_cache  [num_pages, page_size, H_kv, d]  dtype, 16-byte aligned

@@ -214,8 +214,8 @@ class Oracle:
         """The keys of a paged cache in sequence order, token-major: for sequence
         b and t = 0 .. len_b - 1, row t % page_size of physical page
         block_table[b][t // page_size] (the page-table indirection the pages pose
-        for a cache split into non-contiguous pages: KingOfEgg, "Flash Attention
-        (4)", PagedAttention question).  cache [num_pages, page_size, H_kv, d]
+        for a cache split into non-contiguous pages: Ringi, "Lecture 25", section
+        8.3, the PagedAttention question).  cache [num_pages, page_size, H_kv, d]
         -> [sum(len_b), H_kv, d]."""
         page_size = cache.shape[1]
         table = np.asarray(block_table, dtype=np.int64)

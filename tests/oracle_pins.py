@@ -11,8 +11,9 @@ Sources for the facts used here:
   explained", section 5.1 (causal mask, -inf before softmax) and its forward
   pseudocode (L = m + log l);  LLM Infra Atlas "FA2: parallelism", section 4
   (causal bound offset by seqlen_k - seqlen_q);  KingOfEgg "Flash Attention (4)",
-  section 3.5 (empty row: inv_sum = 1 so O = 0), and its PagedAttention question
-  (a K/V cache in non-contiguous pages reached through a page table).
+  section 3.5 (empty row: inv_sum = 1 so O = 0);  Ringi, "Lecture 25", section 8.3
+  (the PagedAttention question: a K/V cache in non-contiguous pages reached
+  through a page table).
 """
 import json
 import math
@@ -497,7 +498,7 @@ def pin_bwd_rows(orc):
     _close(sv, dv.reshape(-1, d)[kr], 0.0, "bwd selected dV rows")
 
 
-# -- paged K/V cache (KingOfEgg, "Flash Attention (4)", PagedAttention question) --
+# -- paged K/V cache (Ringi, "Lecture 25", section 8.3, PagedAttention question) --
 def _paged_from_contiguous(k, lens, page_size, order):
     """Pin-side paging of contiguous k [B, H_kv, N, d]: sequence b's logical page j
     goes to physical page order[next free]; returns the cache [P, page_size,
