@@ -608,6 +608,96 @@ def pin_paged_splits(orc):
     _close(lc.reshape(H), lse[0], 1e-12, "paged combined LSE")
 
 
+# -- FP8 (e4m3) inputs with per-block scales (Ringi, "Lecture 25", section 5.4) --
+def pin_e4m3_decode(orc=None):
+    """Values the e4m3 format definition fixes (OCP 8-bit floating point, E4M3FN:
+    bias 7, 3 mantissa bits, subnormals m * 2^-9, S.1111.111 NaN, max 448)."""
+    from oracle import fp8
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+             0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for code, val in known.items():
+        got = float(fp8.decode_e4m3(np.array([code], dtype=np.uint8))[0])
+        assert got == val, f"e4m3 0x{code:02x} decodes to {got}, not {val}"
+    assert np.isnan(fp8.decode_e4m3(np.array([0x7F, 0xFF], dtype=np.uint8))).all(), "e4m3 NaN patterns"
+    pos = fp8.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0), "e4m3 positive values must increase with the code"
+
+
+def pin_e4m3_encode(orc=None):
+    """Round to nearest, ties to the even code: every finite value maps back to
+    its code, midpoints to the even neighbour, points just off a midpoint to the
+    nearer one; the sign bit follows the input."""
+    from oracle import fp8
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = fp8.decode_e4m3(codes)
+    assert np.array_equal(fp8.encode_e4m3(vals), codes), "e4m3 round trip"
+    pos = fp8.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    mid = (pos[1:] + pos[:-1]) / 2
+    lo_code = np.arange(0x7E)
+    even = np.where(lo_code % 2 == 0, lo_code, lo_code + 1)
+    assert np.array_equal(fp8.encode_e4m3(mid), even.astype(np.uint8)), "e4m3 ties to even"
+    eps = (pos[1:] - pos[:-1]) * 1e-6
+    assert np.array_equal(fp8.encode_e4m3(mid - eps), lo_code.astype(np.uint8)), "e4m3 below a midpoint"
+    assert np.array_equal(fp8.encode_e4m3(mid + eps), (lo_code + 1).astype(np.uint8)), "e4m3 above a midpoint"
+    assert np.array_equal(fp8.encode_e4m3(-mid[10:20]), even[10:20].astype(np.uint8) | 0x80), "e4m3 sign"
+
+
+def pin_fp8_quantize_blocks(orc=None):
+    """Per-block quantization: descale = amax / 448, the largest element of a
+    block maps to +-448, every value lands within the e4m3 rounding of the
+    original, an all-zero block gets descale 1."""
+    from oracle import fp8
+    x = _rand((2, 300, 16), torch.bfloat16, 541) * 3
+    x[1, 256:] = 0
+    codes, dsc = fp8.quantize_blocks(x, 128)
+    assert codes.shape == (2, 300, 16) and dsc.shape == (2, 3)
+    xf = x.float().numpy()
+    for g in range(2):
+        for b in range(3):
+            blk = xf[g, b * 128:(b + 1) * 128]
+            amax = np.float32(np.abs(blk).max())
+            if amax == 0:
+                assert dsc[g, b] == 1.0 and not codes[g, b * 128:(b + 1) * 128].any(), "zero block"
+                continue
+            assert dsc[g, b] == amax / np.float32(448.0), f"descale of block ({g}, {b})"
+            k = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
+            assert codes[g, b * 128 + k[0], k[1]] & 0x7F == 0x7E, "block maximum must reach 448"
+    deq = fp8.dequantize(codes, dsc, 128)
+    # e4m3 unit roundoff 2^-4 for normals; below 2^-6 * descale the spacing is 2^-9 * descale
+    tol = np.maximum(np.abs(xf) * 2.0 ** -4, 2.0 ** -10 * dsc.astype(np.float64)[:, np.arange(300) // 128][:, :, None])
+    assert np.all(np.abs(deq - xf) <= tol * (1 + 1e-6)), "quantized values off by more than the e4m3 rounding"
+
+
+def pin_fp8_attention_matches_fp16(orc):
+    """With power-of-two scales every dequantized e4m3 value is exact in fp16, so
+    FP8 attention must equal the fp16 oracle on those values (per-block Q and K
+    scales, per-head V scales, grouped heads, causal with Nq != Nk)."""
+    from oracle import fp8
+    B, H, H_kv, Nq, Nk, d = 1, 4, 2, 200, 260, 16
+    g = torch.Generator().manual_seed(551)
+    small = np.array([c for c in range(256) if abs(fp8.decode_e4m3(np.array([c], np.uint8))[0]) <= 2.0],
+                     dtype=np.uint8)
+    pick = lambda shape: small[torch.randint(0, small.size, shape, generator=g).numpy()]   # noqa: E731
+    q8, k8, v8 = pick((B, H, Nq, d)), pick((B, H_kv, Nk, d)), pick((B, H_kv, Nk, d))
+    pw = np.array([2.0 ** -3, 0.5, 1.0, 4.0], dtype=np.float32)
+    qd = pw[torch.randint(0, 4, (B, H, 2), generator=g).numpy()]
+    kd = pw[torch.randint(0, 4, (B, H_kv, 3), generator=g).numpy()]
+    vd = pw[torch.randint(0, 4, (B, H_kv), generator=g).numpy()]
+    qx = fp8.dequantize(q8.reshape(B * H, Nq, d), qd.reshape(B * H, 2), 128).reshape(B, H, Nq, d)
+    kx = fp8.dequantize(k8.reshape(B * H_kv, Nk, d), kd.reshape(B * H_kv, 3), 128).reshape(B, H_kv, Nk, d)
+    vx = fp8.decode_e4m3(v8) * vd[:, :, None, None]
+    q16, k16, v16 = (torch.from_numpy(t).half() for t in (qx, kx, vx))
+    assert np.array_equal(q16.double().numpy(), qx) and np.array_equal(v16.double().numpy(), vx), "not exact in fp16"
+    for causal in (False, True):
+        o, lse, amag = fp8.attention_fp8(q8, k8, v8, qd, kd, vd, causal, 0.3)
+        ro, rl = orc.attention_gqa(q16, k16, v16, causal, 0.3, nthreads=2)
+        _close(o, ro, 1e-12, f"fp8 attention O causal={causal}")
+        _close(lse, rl, 1e-12, f"fp8 attention LSE causal={causal}")
+        assert np.all(amag + 1e-12 >= np.abs(o)), "sum p|v|/l bounds |O|"
+
+
+FP8_PINS = [pin_e4m3_decode, pin_e4m3_encode, pin_fp8_quantize_blocks, pin_fp8_attention_matches_fp16]
+
 ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,

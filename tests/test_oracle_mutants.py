@@ -119,3 +119,60 @@ def test_paged_gather_mutants_are_caught(kind):
         except (AssertionError, IndexError, RuntimeError):
             caught += 1
     assert caught, f"no paged pin catches the {kind} mutant"
+
+
+FP8_MUTANTS = {
+    # decoder: exponent bias 8 instead of 7
+    "decode_bias": ("normal = sign * np.ldexp(1.0 + mant / 8.0, expo - 7)",
+                    "normal = sign * np.ldexp(1.0 + mant / 8.0, expo - 8)"),
+    # decoder: subnormals scaled as 2^-10
+    "decode_subnormal": ("sub = sign * np.ldexp(mant.astype(np.float64), -9)",
+                         "sub = sign * np.ldexp(mant.astype(np.float64), -10)"),
+    # encoder: ties away from zero
+    "encode_ties_away": ("pick = np.where(tie & (lo != hi), np.where(hi % 2 == 0, hi, lo), pick)",
+                         "pick = np.where(tie & (lo != hi), hi, pick)"),
+    # quantizer: descale of the block taken as 448 / amax
+    "descale_inverted": ("descale[g, b] = amax / np.float32(E4M3_MAX)",
+                         "descale[g, b] = np.float32(E4M3_MAX) / amax"),
+    # attention: K scale looked up per 64 keys
+    "k_block": ("kx = dequantize(k8[b, hk][None], kd[b, hk][None], K_BLOCK)[0]",
+                "kx = dequantize(k8[b, hk][None], kd[b, hk][None], 64)[0]"),
+    # attention: V scale ignored
+    "v_scale": ("vx = decode_e4m3(v8[b, hk]) * float(vd[b, hk])", "vx = decode_e4m3(v8[b, hk])"),
+    # attention: causal bound off by one
+    "causal": ("hi = Nk if not causal else max(0, min(Nk, i + (Nk - Nq) + 1))",
+               "hi = Nk if not causal else max(0, min(Nk, i + (Nk - Nq)))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_oracle_mutants_are_caught(name, tmp_path, oracle_lib):
+    """Plausible mistakes in the FP8 oracle (decoder, encoder, quantizer,
+    scales, mask) each fail at least one FP8 pin."""
+    import importlib.util
+    from oracle import fp8
+    old, new = FP8_MUTANTS[name]
+    src = open(fp8.__file__).read()
+    assert src.count(old) == 1, f"pattern for {name} must occur exactly once"
+    path = tmp_path / f"fp8_{name}.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"fp8_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    import sys
+    saved = sys.modules.get("oracle.fp8")
+    import oracle as oracle_pkg
+    saved_attr = getattr(oracle_pkg, "fp8", None)
+    sys.modules["oracle.fp8"] = mod
+    oracle_pkg.fp8 = mod
+    caught = []
+    try:
+        for pin in oracle_pins.FP8_PINS:
+            try:
+                pin(oracle_lib)
+            except (AssertionError, ValueError, IndexError) as e:
+                caught.append(f"{pin.__name__}: {str(e)[:60]}")
+    finally:
+        sys.modules["oracle.fp8"] = saved
+        oracle_pkg.fp8 = saved_attr
+    assert caught, f"no FP8 pin catches the mutant {name}"
