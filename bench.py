@@ -9,6 +9,8 @@ One step = one pass of the whole path over resident synthetic inputs:
     a paged cache of 16-row pages scattered by a seeded permutation
     (decode_paged), and
   * bwd: fa_bwd on the long-context causal workload (dO ~ N(0,1)), and
+  * fp8: fa_fwd_fp8 on the long-context workload's inputs quantized to e4m3
+    per block (untimed), and
   * varlen: fa_fwd_varlen on 16 packed causal sequences (lengths log-uniform in
     [64, 8192], 20752 tokens) with 32 query heads sharing 8 K/V heads, d=128, bf16.
 `value` is the prefill throughput in TFLOP/s with FLOPs = 4*B*H*Nq*Nk*d, halved
@@ -39,6 +41,7 @@ from exact_attention_22_amd.inputs import BY_NAME, make_paged, make_qkv, make_va
 METRIC = "attn fwd TFLOPS & % MFMA peak (fp16 d=128 causal N=8K); decode HBM GB/s"
 PEAK_TFLOPS = {torch.bfloat16: 2500.0, torch.float16: 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 FWD_SOURCES = ["exact_attention_22_amd/csrc/fa_fwd.hip", "exact_attention_22_amd/csrc/fa_device.h"]
 DEC_SOURCES = ["exact_attention_22_amd/csrc/fa_decode.hip", "exact_attention_22_amd/csrc/fa_device.h"]
@@ -107,7 +110,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa", "decode_paged", "bwd"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "varlen", "decode_gqa", "decode_paged", "bwd", "fp8"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=40000)
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -129,6 +132,7 @@ def main():
     do_g = args.only in ("all", "decode_gqa")
     do_b = args.only in ("all", "bwd")
     do_pg = args.only in ("all", "decode_paged")
+    do_f8 = args.only in ("all", "fp8")
     wpg = BY_NAME["decode_paged"]
     if do_p:
         q, k, v = make_qkv(wp, device=dev)
@@ -171,6 +175,17 @@ def main():
         plp = torch.empty((wpg.splits, wpg.B, wpg.H, 1), dtype=torch.float32, device=dev)
         po = torch.empty((wpg.B, wpg.H, 1, wpg.d), dtype=wpg.dtype, device=dev)
         plse = torch.empty((wpg.B, wpg.H, 1), dtype=torch.float32, device=dev)
+    if do_f8:
+        # long_causal's inputs quantized per block (Q, K: 128 rows; V: per head), untimed
+        fq, fk, fv = make_qkv(wp, device=dev)
+        G = wp.B * wp.H
+        f8 = [fa.quantize_fp8(t.reshape(G, wp.Nq, wp.d), br) for t, br in ((fq, 128), (fk, 128), (fv, wp.Nk))]
+        del fq, fk, fv
+        fq8, fk8, fv8 = (c.reshape(wp.B, wp.H, wp.Nq, wp.d) for c, _ in f8)
+        fqd, fkd = f8[0][1].reshape(wp.B, wp.H, -1), f8[1][1].reshape(wp.B, wp.H, -1)
+        fvd = f8[2][1].reshape(wp.B, wp.H)
+        fo = torch.empty((wp.B, wp.H, wp.Nq, wp.d), dtype=torch.bfloat16, device=dev)
+        flse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device=dev)
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -183,7 +198,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e = [ev() for _ in range(10)]
+        e = [ev() for _ in range(11)]
         e[0].record(stream)
         if do_p:
             fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse, stream=stream)
@@ -217,6 +232,9 @@ def main():
         if do_pg:
             fa.splitkv_combine(pop, plp, wpg.dtype, out=po, lse=plse, stream=stream)
         e[9].record(stream)
+        if do_f8:
+            fa.fwd_fp8(fq8, fk8, fv8, fqd, fkd, fvd, causal=wp.causal, scale=wp.scale, out=fo, lse=flse, stream=stream)
+        e[10].record(stream)
         if rec is not None:
             rec.append(e)
 
@@ -237,6 +255,7 @@ def main():
     t_gsplit, t_gcomb = avg_ms(4, 5), avg_ms(5, 6)
     t_bwd = avg_ms(6, 7)
     t_psplit, t_pcomb = avg_ms(7, 8), avg_ms(8, 9)
+    t_f8 = avg_ms(9, 10)
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic"}
@@ -340,6 +359,19 @@ def main():
         if args.only == "decode_paged":
             out.update({"value": out["decode_paged"]["GB_per_s"], "unit": "GB/s", "dtype": "f16"})
             cfg["workload"] = "decode_paged: B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 fp16 16 splits, 16-row pages"
+    if do_f8:
+        fl = attn_flops(wp.B, wp.H, wp.Nq, wp.Nk, wp.d, wp.causal)
+        t8 = fl / (t_f8 * 1e-3) / 1e12
+        out["fp8"] = {"TFLOP_per_s": t8, "pct_mfma_peak": 100.0 * t8 / PEAK_FP8_TFLOPS, "avg_us": t_f8 * 1e3,
+                      "flop_per_launch": fl}
+        out["roofline_fp8"] = {"bound": "mfma", "achieved": t8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                               "frac": t8 / PEAK_FP8_TFLOPS, "traffic": None,
+                               "kernel": "fwd_fp8_kernel<e4m3, d=128, causal>"}
+        cfg["fp8"] = {"B": wp.B, "H": wp.H, "Nq": wp.Nq, "Nk": wp.Nk, "d": wp.d, "dtype": "e4m3 in, bf16 out",
+                      "causal": True, "scales": "Q, K per 128 rows; V per head"}
+        if args.only == "fp8":
+            out.update({"value": t8, "unit": "TFLOP/s", "dtype": "fp8"})
+            cfg["workload"] = "fp8 on long_causal: B=1 H=32 Nq=Nk=8192 d=128 e4m3 causal"
     out["config"] = cfg
     if do_p and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(q, k, v, wp, args.cpu_rows)

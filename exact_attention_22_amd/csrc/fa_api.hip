@@ -187,6 +187,34 @@ fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v
     return from_hip(fa::launch_decode(p, (hipStream_t)stream));
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                     const float* k_descale, const float* v_descale, void* o, float* lse,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+    if (!q || !k || !v || !q_descale || !k_descale || !v_descale || !o || !lse) return FA_ERR_NULL;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+    if (check_heads(H, H_kv) != FA_OK) return FA_ERR_SHAPE;
+    if (count4(B, H, Nq, d) < 0 || count4(B, H_kv, Nk, d) < 0 || (int64_t)B * H > INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u) ||
+        ((uintptr_t)q_descale & 3u) || ((uintptr_t)k_descale & 3u) || ((uintptr_t)v_descale & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::Fp8Params p{q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, H_kv, Nq, Nk, causal != 0, scale};
+    return from_hip(fa::launch_fwd_fp8(p, (hipStream_t)stream));
+}
+
+fa_status fa_quantize_fp8(const void* x, void* x8, float* descale, int G, int N, int d, int block_rows,
+                          fa_dtype dtype, void* stream) {
+    if (!x || !x8 || !descale) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d < 8 || d % 8 != 0) return FA_ERR_UNSUPPORTED;
+    if (G < 1 || N < 1 || block_rows < 1 || count4(G, N, d, 1) < 0) return FA_ERR_SHAPE;
+    if ((int64_t)G * ((N + (int64_t)block_rows - 1) / block_rows) > INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(x8) || ((uintptr_t)descale & 3u)) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_quant_fp8(x, x8, descale, G, N, d, block_rows, dtype == FA_BF16,
+                                         (hipStream_t)stream));
+}
+
 fa_status fa_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                              int B, int H, int Nq, int d, int num_splits, fa_dtype dtype, void* stream) {
     if (!o_part || !lse_part || !o || !lse) return FA_ERR_NULL;

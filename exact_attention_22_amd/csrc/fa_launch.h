@@ -53,7 +53,28 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+// Validated arguments of one FP8 forward: e4m3 q [B, H, Nq, 128], k and v
+// [B, H_kv, Nk, 128]; descales q [B, H, ceil(Nq/128)], k [B, H_kv,
+// ceil(Nk/128)], v [B, H_kv]; o bf16 [B, H, Nq, 128], lse [B, H, Nq].
+struct Fp8Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* q_descale;
+    const float* k_descale;
+    const float* v_descale;
+    void* o;
+    float* lse;
+    int B, H, H_kv, Nq, Nk;
+    bool causal;
+    float scale;
+};
+
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
+// x [G, N, d] 16-bit -> e4m3 codes [G, N, d] and descale [G, ceil(N / rows)]
+hipError_t launch_quant_fp8(const void* x, void* x8, float* descale, int64_t G, int N, int d, int rows,
+                            bool bf16, hipStream_t stream);
 hipError_t launch_decode(const FwdParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                           int64_t rows, int d, int num_splits, bool bf16, hipStream_t stream);

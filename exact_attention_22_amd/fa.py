@@ -18,7 +18,7 @@ FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_status_str")
+           "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -57,6 +57,10 @@ def lib():
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
         L.fa_bwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, f, i, vp]
+        L.fa_fwd_fp8.restype = i
+        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        L.fa_quantize_fp8.restype = i
+        L.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [i]
         _lib = L
@@ -310,3 +314,61 @@ def decode(q, k, v, num_splits=16, causal=False, scale=None, stream=None, o_part
     split = fwd_splitkv_gqa if k.dim() == 4 and q.dim() == 4 and k.shape[1] != q.shape[1] else fwd_splitkv
     o_part, lse_part = split(q, k, v, num_splits, causal, scale, o_part, lse_part, stream)
     return splitkv_combine(o_part, lse_part, q.dtype, stream=stream)
+
+
+FP8_BLOCK = 128   # rows per Q scale and per K scale of fwd_fp8
+
+
+def _codes(t, name):
+    """uint8 (or float8_e4m3fn, viewed as bytes) GPU tensor -> pointer."""
+    if isinstance(t, torch.Tensor) and t.dtype == getattr(torch, "float8_e4m3fn", None):
+        t = t.view(torch.uint8)
+    return _dev_tensor(t, name, torch.uint8)
+
+
+def quantize_fp8(x, block_rows, out=None, descale=None, stream=None):
+    """Per-block e4m3 quantization of x [G, N, d] (fp16/bf16): returns codes
+    (uint8 [G, N, d]) and descale (fp32 [G, ceil(N / block_rows)])."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    if x.dim() != 3:
+        raise ValueError("x must be [G, N, d]")
+    G, N, d = x.shape
+    nb = -(-N // int(block_rows))
+    out = torch.empty((G, N, d), dtype=torch.uint8, device=x.device) if out is None else out
+    descale = torch.empty((G, nb), dtype=torch.float32, device=x.device) if descale is None else descale
+    if tuple(out.shape) != (G, N, d) or tuple(descale.shape) != (G, nb):
+        raise ValueError("out must be [G, N, d] and descale [G, ceil(N / block_rows)]")
+    _check(lib().fa_quantize_fp8(_dev_tensor(x, "x", x.dtype), _codes(out, "out"),
+                                 _dev_tensor(descale, "descale", torch.float32), G, N, d, int(block_rows),
+                                 _DTYPES[x.dtype], _stream(stream)))
+    return out, descale
+
+
+def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=None, out=None, lse=None,
+            stream=None):
+    """FP8 forward: e4m3 codes q8 [B, H, Nq, 128], k8 and v8 [B, H_kv, Nk, 128];
+    descales q [B, H, ceil(Nq/128)], k [B, H_kv, ceil(Nk/128)], v [B, H_kv] (fp32).
+    Returns O (bf16 [B, H, Nq, 128]) and LSE (fp32 [B, H, Nq])."""
+    if q8.dim() != 4 or k8.dim() != 4 or v8.dim() != 4:
+        raise ValueError("q8, k8, v8 must be [B, H, N, d]")
+    B, H, Nq, d = q8.shape
+    H_kv, Nk = k8.shape[1], k8.shape[2]
+    if tuple(k8.shape) != (B, H_kv, Nk, d) or tuple(v8.shape) != (B, H_kv, Nk, d):
+        raise ValueError("k8 and v8 must be [B, H_kv, Nk, d] with q8's B and d")
+    nq, nk = -(-Nq // FP8_BLOCK), -(-Nk // FP8_BLOCK)
+    if (tuple(q_descale.shape) != (B, H, nq) or tuple(k_descale.shape) != (B, H_kv, nk)
+            or tuple(v_descale.shape) != (B, H_kv)):
+        raise ValueError("descales must be q [B, H, ceil(Nq/128)], k [B, H_kv, ceil(Nk/128)], v [B, H_kv]")
+    ptrs = [_codes(t, n) for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8"))]
+    dps = [_dev_tensor(t, n, torch.float32) for t, n in ((q_descale, "q_descale"), (k_descale, "k_descale"),
+                                                         (v_descale, "v_descale"))]
+    out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device) if lse is None else lse
+    if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("out must be [B, H, Nq, d] and lse [B, H, Nq]")
+    op = _dev_tensor(out, "out", torch.bfloat16)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    _check(lib().fa_fwd_fp8(*ptrs, *dps, op, lp, B, H, H_kv, Nq, Nk, d, int(bool(causal)), _scale(scale, d),
+                            _stream(stream)))
+    return out, lse

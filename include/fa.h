@@ -177,6 +177,40 @@ fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v
                                float scale, int num_splits, fa_dtype dtype, void* stream);
 
 /*
+ * FP8 forward (Ringi, "Lecture 25", section 5.4: Q K^T and P V on FP8 operands
+ * with per-block scale factors): O and LSE of attention on the dequantized
+ * inputs x = code * descale, where
+ *   q        [B, H, Nq, d]     e4m3 codes (OCP E4M3FN bytes), 16-byte aligned
+ *   k, v     [B, H_kv, Nk, d]  e4m3 codes, 16-byte aligned
+ *   q_descale [B, H, ceil(Nq / 128)]     fp32: one per 128 query rows
+ *   k_descale [B, H_kv, ceil(Nk / 128)]  fp32: one per 128 keys
+ *   v_descale [B, H_kv]                  fp32: one per K/V head
+ *   o        [B, H, Nq, d]     bfloat16;  lse [B, H, Nq] fp32 (natural log of the
+ *            scaled scores of the dequantized inputs)
+ * Query head h reads K/V head h / (H / H_kv); causal alignment and scale as
+ * fa_fwd.  P is rounded to e4m3 (after a per-row power-of-two lift that keeps
+ * the largest weights at the top of the e4m3 range) before its product with V;
+ * its row sum is kept in fp32.  d must be 128.  Descales must be finite and
+ * positive (fa_quantize_fp8 produces them).
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                     const float* k_descale, const float* v_descale, void* o, float* lse,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, void* stream);
+
+/*
+ * Block quantizer for fa_fwd_fp8's inputs (the per-block scale factors of
+ * Ringi, "Lecture 25", section 5.4): x [G, N, d] fp16/bf16 -> codes [G, N, d]
+ * (e4m3 bytes) and descale [G, ceil(N / block_rows)] fp32.  Per block of
+ * block_rows rows: amax = max |x|; descale = amax / 448 (1 for an all-zero
+ * block); code = the e4m3 value nearest x * (448 / amax) (fp32 arithmetic,
+ * clamped to +-448, ties to even).  For fa_fwd_fp8 use block_rows = 128 for q
+ * and k (G = B*H or B*H_kv) and block_rows = N for v.  d a multiple of 8; x and
+ * codes 16-byte aligned.  Inputs must be finite.
+ */
+fa_status fa_quantize_fp8(const void* x, void* x8, float* descale, int G, int N, int d, int block_rows,
+                          fa_dtype dtype, void* stream);
+
+/*
  * Split-KV forward, second half: merge the partials with the online-softmax
  * identity (Ringi, Lecture 25, section 2.2).  Per row:
  *   M = max_s lse_part[s];  w_s = exp(lse_part[s] - M) (0 for -inf);

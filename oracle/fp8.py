@@ -113,8 +113,13 @@ def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, ro
     (float32).  Query head h reads K/V head h // (H // H_kv); causal key j is
     visible to query i iff j <= i + Nk - Nq.  rows: optional flat indices
     (b*H + h)*Nq + i; then o is [len(rows), d] and lse [len(rows)], else o
-    [B, H, Nq, d] and lse [B, H, Nq].  Also returns, for the error bound of the
-    kernel's FP8 P, A[r, t] = sum_j p_j |v_jt| / l (same shape as o).
+    [B, H, Nq, d] and lse [B, H, Nq].
+
+    Also returns, for the error bound of a kernel that rounds P to e4m3, two
+    arrays shaped like o: A[r, t] = sum_j p_j |v_jt| / l (the weight-averaged
+    magnitude) and U[r, t] = sum over keys with p_j / max p < 2^-10 of |v_jt|,
+    divided by l (the magnitude carried by weights small enough to reach e4m3's
+    subnormal range); p_j = exp(s_j - m).
     """
     q8, k8, v8 = (np.asarray(t, dtype=np.uint8) for t in (q8, k8, v8))
     B, H, Nq, d = q8.shape
@@ -128,6 +133,7 @@ def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, ro
     o = np.zeros((flat.size, d))
     lse = np.full(flat.size, -np.inf)
     amag = np.zeros((flat.size, d))
+    umag = np.zeros((flat.size, d))
     cache = {}
     for r, f in enumerate(flat):
         bh, i = divmod(int(f), Nq)
@@ -149,6 +155,8 @@ def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, ro
         o[r] = (p @ vx[:hi]) / l
         lse[r] = m + math.log(l)
         amag[r] = (p @ np.abs(vx[:hi])) / l
+        umag[r] = np.abs(vx[:hi])[p < 2.0 ** -10].sum(axis=0) / l
     if rows is None:
-        return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq), amag.reshape(B, H, Nq, d)
-    return o, lse, amag
+        sh = (B, H, Nq, d)
+        return o.reshape(sh), lse.reshape(B, H, Nq), amag.reshape(sh), umag.reshape(sh)
+    return o, lse, amag, umag

@@ -689,7 +689,7 @@ def pin_fp8_attention_matches_fp16(orc):
     q16, k16, v16 = (torch.from_numpy(t).half() for t in (qx, kx, vx))
     assert np.array_equal(q16.double().numpy(), qx) and np.array_equal(v16.double().numpy(), vx), "not exact in fp16"
     for causal in (False, True):
-        o, lse, amag = fp8.attention_fp8(q8, k8, v8, qd, kd, vd, causal, 0.3)
+        o, lse, amag, _ = fp8.attention_fp8(q8, k8, v8, qd, kd, vd, causal, 0.3)
         ro, rl = orc.attention_gqa(q16, k16, v16, causal, 0.3, nthreads=2)
         _close(o, ro, 1e-12, f"fp8 attention O causal={causal}")
         _close(lse, rl, 1e-12, f"fp8 attention LSE causal={causal}")

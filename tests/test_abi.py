@@ -174,6 +174,36 @@ def test_paged_validation():
     assert paged(sl=ctypes.c_void_p(0x10001)) == fa.FA_ERR_UNSUPPORTED
 
 
+def fwd8(q=A, k=A, v=A, qd=A, kd=A, vd=A, o=A, lse=A, B=1, H=4, H_kv=2, Nq=128, Nk=128, d=128, causal=1,
+         scale=0.1):
+    return fa.lib().fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, H, H_kv, Nq, Nk, d, causal, scale, NULL)
+
+
+def quant8(x=A, x8=A, dsc=A, G=2, N=100, d=128, br=128, dtype=1):
+    return fa.lib().fa_quantize_fp8(x, x8, dsc, G, N, d, br, dtype, NULL)
+
+
+def test_fp8_validation():
+    for kw in ("q", "k", "v", "qd", "kd", "vd", "o", "lse"):
+        assert fwd8(**{kw: NULL}) == fa.FA_ERR_NULL, kw
+    assert fwd8(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(B=0) == fa.FA_ERR_SHAPE
+    assert fwd8(Nk=0) == fa.FA_ERR_SHAPE
+    assert fwd8(H=4, H_kv=3) == fa.FA_ERR_SHAPE
+    assert fwd8(q=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(o=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(kd=ctypes.c_void_p(0x10002)) == fa.FA_ERR_UNSUPPORTED
+    for kw in ("x", "x8", "dsc"):
+        assert quant8(**{kw: NULL}) == fa.FA_ERR_NULL, kw
+    assert quant8(dtype=3) == fa.FA_ERR_UNSUPPORTED
+    assert quant8(d=12) == fa.FA_ERR_UNSUPPORTED
+    assert quant8(G=0) == fa.FA_ERR_SHAPE
+    assert quant8(br=0) == fa.FA_ERR_SHAPE
+    assert quant8(x=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert quant8(x8=MIS) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_combine_validation():
     assert combine(lp=NULL) == fa.FA_ERR_NULL
     assert combine(S=0) == fa.FA_ERR_SHAPE
