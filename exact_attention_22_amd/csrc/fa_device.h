@@ -66,6 +66,10 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
         (__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// Larger of two floats, NaN if either is NaN (v_maximum3_f32 on gfx950).  Unlike
+// fmaxf it needs no canonicalisation of matrix-core results first.
+__device__ __forceinline__ float fmax_raw(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Sum / max of a value over lanes l and l^32 (v_permlane32_swap: every lane
 // ends with both halves' values).
 __device__ __forceinline__ float sum_halves(float x) {
@@ -74,7 +78,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 __device__ __forceinline__ float max_halves(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[kb][r]);
         mx = max_halves(mx);
         const float Mc = (mx == -INFINITY) ? -INFINITY : mx * c;
         if (__ballot(Mc > Mu + F8_TAU)) {        // wave-uniform: move the reference

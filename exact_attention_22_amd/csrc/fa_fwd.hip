@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int qw = q0 + 32 * w;
@@ -266,9 +266,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         // row max over this tile (raw scores), both lane halves
         float mx = sacc[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+        for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sacc[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[1][r]);
         mx = max_halves(mx);
         const float Mc = (mx == -INFINITY) ? -INFINITY : mx * a.c;
         if (__ballot(Mc > Mu + TAU)) {          // wave-uniform: move the reference
