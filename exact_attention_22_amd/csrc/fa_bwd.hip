@@ -147,14 +147,32 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW]) {
     }
 }
 
-// Work item from blockIdx: XCD-contiguous ranges (tiles of one head share an
-// XCD's L2), `per_head` tiles per head, tile index in the order given.
-__device__ __forceinline__ void work_item(int per_head, int BH, int& tile, int& bh) {
+// Work items of this workgroup: XCD-contiguous ranges (tiles of one head share
+// an XCD's L2), `per_head` tiles per head, tile index in the order given (the
+// longest causal tile first).  PAIR (causal): the workgroup runs tiles t and
+// per_head-1-t, which together carry a fixed amount of work, so the XCD
+// round-robin dispatcher never stalls on one XCD's long tile.
+template <bool PAIR, class F>
+__device__ __forceinline__ void for_items(int per_head, int BH, F&& item) {
     const int total = gridDim.x;
     int L = blockIdx.x;
     if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-    tile = L % per_head;
-    bh = (L / per_head) % BH;
+    if (PAIR && per_head >= 2) {
+        const int npairs = (per_head + 1) >> 1;
+        const int t = L % npairs, bh = L / npairs;
+        item(t, bh);
+        if (t != per_head - 1 - t) {
+            __syncthreads();        // the next item refills the LDS stages
+            item(per_head - 1 - t, bh);
+        }
+    } else {
+        item(L % per_head, (L / per_head) % BH);
+    }
+}
+
+// Workgroups of a launch over `per_head` tiles per head (see for_items).
+inline int64_t item_blocks(bool pair, int per_head, int BH) {
+    return (pair && per_head >= 2) ? (int64_t)((per_head + 1) / 2) * BH : (int64_t)per_head * BH;
 }
 
 // Two score products over one 32-row block of LDS tiles: S = A1 B1 and
@@ -222,106 +240,107 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];   // [K | V]
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
-    int t, bh;
-    work_item(a.n_qtiles, a.BH, t, bh);
-    const int qt = a.n_qtiles - 1 - t;                   // longest causal rows first
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
-    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-    const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
-    const uint16_t* kg = a.k + (size_t)bh * Nk * D;
-    const uint16_t* vg = a.v + (size_t)bh * Nk * D;
+    auto run_item = [&](const int t, const int bh) __attribute__((always_inline)) {
+        const int qt = a.n_qtiles - 1 - t;               // longest causal rows first
+        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
+        const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+        const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
+        const uint16_t* kg = a.k + (size_t)bh * Nk * D;
+        const uint16_t* vg = a.v + (size_t)bh * Nk * D;
 
-    int hi = Nk;
-    if (CAUSAL) hi = min(hi, min(Nq, q0 + BQ) + off);
-    const int n_tiles = hi > 0 ? (hi + BK - 1) / BK : 0;
+        int hi = Nk;
+        if (CAUSAL) hi = min(hi, min(Nq, q0 + BQ) + off);
+        const int n_tiles = hi > 0 ? (hi + BK - 1) / BK : 0;
 
-    // this lane's query row: Q and dO chunks, LSE (log2 units) and D
-    u32x4 qf[NS], gf[NS];
-    const bool qok = qi < Nq;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const size_t e = ((size_t)bh * Nq + qi) * D + 16 * s + 8 * h;
-        qf[s] = qok ? *(const u32x4*)(a.q + e) : u32x4{0, 0, 0, 0};
-        gf[s] = qok ? *(const u32x4*)(a.dout + e) : u32x4{0, 0, 0, 0};
-    }
-    const float lse2 = qok ? a.lse2[(size_t)bh * Nq + qi] : 0.f;
-    const float dlt = qok ? a.delta[(size_t)bh * Nq + qi] : 0.f;
-
-    u32 voff[NPW];
-    dma_offsets<D, NPW>(w, lane, voff);
-    auto load_tile = [&](int tile, unsigned char* stage) {
-        const int k0 = tile * BK;
-        load_rows<D, NPW>(kg + (size_t)k0 * D, Nk - k0, stage, w, voff);
-        load_rows<D, NPW>(vg + (size_t)k0 * D, Nk - k0, stage + TILE, w, voff);
-    };
-    const Offsets<D> of(lane);
-
-    f32x16 dqacc[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) dqacc[db] = f32x16{};
-
-    // One key tile of two 32-key blocks.  Keys at or past `bound` (relative to
-    // k0 + 8h; the key tail or, causal, past this row's diagonal) get P = 0 in
-    // masked tiles.  The scores of the second block are issued before the first
-    // block's element-wise work.
-    auto step = [&](const unsigned char* Kb, const unsigned char* Vb, int bound, auto mask) {
-        constexpr bool MASK = decltype(mask)::value;
-        f32x16 s0, d0, s1, d1;
-        u32x4 ds0[2], ds1[2];
-        scores<BF16, D>(Kb, Vb, 0, of, qf, gf, s0, d0);
-        scores<BF16, D>(Kb, Vb, 1, of, qf, gf, s1, d1);
-        dq_probs<BF16, MASK>(s0, d0, lse2, dlt, a.c, bound, ds0);
-        dq_accum<BF16, D>(Kb, 0, of, ds0, dqacc);
-        dq_probs<BF16, MASK>(s1, d1, lse2, dlt, a.c, bound - 32, ds1);
-        dq_accum<BF16, D>(Kb, 1, of, ds1, dqacc);
-    };
-
-    // key tiles from the last one down: the ones crossing the diagonal or the key
-    // tail come first
-    int n_masked = 0;
-    while (n_masked < n_tiles) {
-        const int k0 = (n_tiles - 1 - n_masked) * BK;
-        const bool clean = k0 + BK <= Nk && (!CAUSAL || k0 + BK - 1 <= q0 + off);
-        if (clean) break;
-        ++n_masked;
-    }
-    if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // two tiles per trip, so that each step reads one fixed LDS stage
-    auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
-        const int tile = n_tiles - 1 - it;
-        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
-        const int k0 = tile * BK;
-        if (it < n_masked) {
-            if (qw < Nq && (!CAUSAL || k0 <= min(qw + 31, Nq - 1) + off)) {
-                int bound = Nk - k0;
-                if (CAUSAL) bound = min(bound, qi + off - k0 + 1);
-                step(cur, cur + TILE, bound - 8 * h, std::true_type{});
-            }
-        } else {
-            step(cur, cur + TILE, BK, std::false_type{});
+        // this lane's query row: Q and dO chunks, LSE (log2 units) and D
+        u32x4 qf[NS], gf[NS];
+        const bool qok = qi < Nq;
+    #pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const size_t e = ((size_t)bh * Nq + qi) * D + 16 * s + 8 * h;
+            qf[s] = qok ? *(const u32x4*)(a.q + e) : u32x4{0, 0, 0, 0};
+            gf[s] = qok ? *(const u32x4*)(a.dout + e) : u32x4{0, 0, 0, 0};
         }
+        const float lse2 = qok ? a.lse2[(size_t)bh * Nq + qi] : 0.f;
+        const float dlt = qok ? a.delta[(size_t)bh * Nq + qi] : 0.f;
+
+        u32 voff[NPW];
+        dma_offsets<D, NPW>(w, lane, voff);
+        auto load_tile = [&](int tile, unsigned char* stage) {
+            const int k0 = tile * BK;
+            load_rows<D, NPW>(kg + (size_t)k0 * D, Nk - k0, stage, w, voff);
+            load_rows<D, NPW>(vg + (size_t)k0 * D, Nk - k0, stage + TILE, w, voff);
+        };
+        const Offsets<D> of(lane);
+
+        f32x16 dqacc[ND];
+    #pragma unroll
+        for (int db = 0; db < ND; ++db) dqacc[db] = f32x16{};
+
+        // One key tile of two 32-key blocks.  Keys at or past `bound` (relative to
+        // k0 + 8h; the key tail or, causal, past this row's diagonal) get P = 0 in
+        // masked tiles.  The scores of the second block are issued before the first
+        // block's element-wise work.
+        auto step = [&](const unsigned char* Kb, const unsigned char* Vb, int bound, auto mask) {
+            constexpr bool MASK = decltype(mask)::value;
+            f32x16 s0, d0, s1, d1;
+            u32x4 ds0[2], ds1[2];
+            scores<BF16, D>(Kb, Vb, 0, of, qf, gf, s0, d0);
+            scores<BF16, D>(Kb, Vb, 1, of, qf, gf, s1, d1);
+            dq_probs<BF16, MASK>(s0, d0, lse2, dlt, a.c, bound, ds0);
+            dq_accum<BF16, D>(Kb, 0, of, ds0, dqacc);
+            dq_probs<BF16, MASK>(s1, d1, lse2, dlt, a.c, bound - 32, ds1);
+            dq_accum<BF16, D>(Kb, 1, of, ds1, dqacc);
+        };
+
+        // key tiles from the last one down: the ones crossing the diagonal or the key
+        // tail come first
+        int n_masked = 0;
+        while (n_masked < n_tiles) {
+            const int k0 = (n_tiles - 1 - n_masked) * BK;
+            const bool clean = k0 + BK <= Nk && (!CAUSAL || k0 + BK - 1 <= q0 + off);
+            if (clean) break;
+            ++n_masked;
+        }
+        if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-    };
-#pragma clang loop unroll(disable)
-    for (int it = 0; it < n_tiles; it += 2) {
-        one(it, stage0, stage1);
-        if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
-    }
-
-    if (qok) {
-        uint16_t* dst = a.dq + ((size_t)bh * Nq + qi) * D;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
-                const u32x2 v2 = {pack2<BF16>(x[0] * a.scale, x[1] * a.scale), pack2<BF16>(x[2] * a.scale, x[3] * a.scale)};
-                *(u32x2*)(dst + 32 * db + 8 * g + 4 * h) = v2;
+        // two tiles per trip, so that each step reads one fixed LDS stage
+        auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
+            const int tile = n_tiles - 1 - it;
+            if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+            const int k0 = tile * BK;
+            if (it < n_masked) {
+                if (qw < Nq && (!CAUSAL || k0 <= min(qw + 31, Nq - 1) + off)) {
+                    int bound = Nk - k0;
+                    if (CAUSAL) bound = min(bound, qi + off - k0 + 1);
+                    step(cur, cur + TILE, bound - 8 * h, std::true_type{});
+                }
+            } else {
+                step(cur, cur + TILE, BK, std::false_type{});
             }
-    }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+    #pragma clang loop unroll(disable)
+        for (int it = 0; it < n_tiles; it += 2) {
+            one(it, stage0, stage1);
+            if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
+        }
+
+        if (qok) {
+            uint16_t* dst = a.dq + ((size_t)bh * Nq + qi) * D;
+    #pragma unroll
+            for (int db = 0; db < ND; ++db)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
+                    const u32x2 v2 = {pack2<BF16>(x[0] * a.scale, x[1] * a.scale), pack2<BF16>(x[2] * a.scale, x[3] * a.scale)};
+                    *(u32x2*)(dst + 32 * db + 8 * g + 4 * h) = v2;
+                }
+        }
+    };
+    for_items<CAUSAL>(a.n_qtiles, a.BH, run_item);
 }
 
 // ---- dK, dV -------------------------------------------------------------------
@@ -378,124 +397,127 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char stage0[STAGE];
     __shared__ __attribute__((aligned(16))) unsigned char stage1[STAGE];
 
-    int kt, bh;
-    work_item(a.n_ktiles, a.BH, kt, bh);                // key tile 0 first: the longest causal columns
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
-    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-    const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
-    const uint16_t* qg = a.q + (size_t)bh * Nq * D;
-    const uint16_t* gg = a.dout + (size_t)bh * Nq * D;
-    const float* lg = a.lse2 + (size_t)bh * Nq;
-    const float* dg = a.delta + (size_t)bh * Nq;
+    // key tile 0 first: the longest causal columns
+    auto run_item = [&](const int kt, const int bh) __attribute__((always_inline)) {
+        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
+        const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+        const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
+        const uint16_t* qg = a.q + (size_t)bh * Nq * D;
+        const uint16_t* gg = a.dout + (size_t)bh * Nq * D;
+        const float* lg = a.lse2 + (size_t)bh * Nq;
+        const float* dg = a.delta + (size_t)bh * Nq;
 
-    // first query row that sees a key of this block, and the query tiles from it
-    const int q_lo = CAUSAL ? max(0, k0 - off) : 0;
-    const int t0 = q_lo / CQ;
-    const int n_qt = (Nq + CQ - 1) / CQ;
-    const int n_tiles = q_lo < Nq ? n_qt - t0 : 0;
+        // first query row that sees a key of this block, and the query tiles from it
+        const int q_lo = CAUSAL ? max(0, k0 - off) : 0;
+        const int t0 = q_lo / CQ;
+        const int n_qt = (Nq + CQ - 1) / CQ;
+        const int n_tiles = q_lo < Nq ? n_qt - t0 : 0;
 
-    // this lane's key row: K and V chunks (the B operands)
-    u32x4 kf[NS], vf[NS];
-    const bool kok = kj < Nk;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const size_t e = ((size_t)bh * Nk + kj) * D + 16 * s + 8 * h;
-        kf[s] = kok ? *(const u32x4*)(a.k + e) : u32x4{0, 0, 0, 0};
-        vf[s] = kok ? *(const u32x4*)(a.v + e) : u32x4{0, 0, 0, 0};
-    }
+        // this lane's key row: K and V chunks (the B operands)
+        u32x4 kf[NS], vf[NS];
+        const bool kok = kj < Nk;
+    #pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const size_t e = ((size_t)bh * Nk + kj) * D + 16 * s + 8 * h;
+            kf[s] = kok ? *(const u32x4*)(a.k + e) : u32x4{0, 0, 0, 0};
+            vf[s] = kok ? *(const u32x4*)(a.v + e) : u32x4{0, 0, 0, 0};
+        }
 
-    u32 voff[NPW];
-    dma_offsets<D, NPW>(w, lane, voff);
-    auto load_tile = [&](int tile, unsigned char* stage) {
-        const int i0 = tile * CQ;
-        load_rows<D, NPW>(qg + (size_t)i0 * D, Nq - i0, stage, w, voff);
-        load_rows<D, NPW>(gg + (size_t)i0 * D, Nq - i0, stage + QTILE, w, voff);
-        // 64 LSE and 64 D values (256 B each) land at lane*16 of a 1 KiB area;
-        // lanes past 64 rows read zeros
-        const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(Nq - i0, 0), CQ)) * 4;
-        if (w == 0) lds_dma16(buffer_rsrc(lg + i0, nrec), stage + 2 * QTILE, (u32)lane * 16);
-        if (w == 1) lds_dma16(buffer_rsrc(dg + i0, nrec), stage + 2 * QTILE + 1024, (u32)lane * 16);
-    };
-    const Offsets<D> of(lane);
+        u32 voff[NPW];
+        dma_offsets<D, NPW>(w, lane, voff);
+        auto load_tile = [&](int tile, unsigned char* stage) {
+            const int i0 = tile * CQ;
+            load_rows<D, NPW>(qg + (size_t)i0 * D, Nq - i0, stage, w, voff);
+            load_rows<D, NPW>(gg + (size_t)i0 * D, Nq - i0, stage + QTILE, w, voff);
+            // 64 LSE and 64 D values (256 B each) land at lane*16 of a 1 KiB area;
+            // lanes past 64 rows read zeros
+            const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(Nq - i0, 0), CQ)) * 4;
+            if (w == 0) lds_dma16(buffer_rsrc(lg + i0, nrec), stage + 2 * QTILE, (u32)lane * 16);
+            if (w == 1) lds_dma16(buffer_rsrc(dg + i0, nrec), stage + 2 * QTILE + 1024, (u32)lane * 16);
+        };
+        const Offsets<D> of(lane);
 
-    f32x16 dkacc[ND], dvacc[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-        dkacc[db] = f32x16{};
-        dvacc[db] = f32x16{};
-    }
+        f32x16 dkacc[ND], dvacc[ND];
+    #pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            dkacc[db] = f32x16{};
+            dvacc[db] = f32x16{};
+        }
 
-    // One query tile of two 32-row blocks.  The scores of the second block are
-    // issued before the first block's element-wise work, which then runs beside
-    // those matrix instructions.
-    auto step = [&](const unsigned char* st, int i0, auto mask) {
-        constexpr bool MASK = decltype(mask)::value;
-        const unsigned char* Qb = st;
-        const unsigned char* Gb = st + QTILE;
-        const float* Ls = (const float*)(st + 2 * QTILE);
-        const float* Ds = (const float*)(st + 2 * QTILE + 1024);
-        const int lim = kj - i0 - off - 8 * h;
-        f32x16 s0, d0, s1, d1;
-        u32x4 pb[2], sb[2];
-        // scheduling fences keep the compiler to these four phases
-        scores<BF16, D>(Qb, Gb, 0, of, kf, vf, s0, d0);
-        __builtin_amdgcn_sched_barrier(0);
-        scores<BF16, D>(Qb, Gb, 1, of, kf, vf, s1, d1);
-        dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_accum<BF16, D>(Qb, Gb, 0, of, pb, sb, dkacc, dvacc);
-        u32x4 pb1[2], sb1[2];
-        dkdv_probs<BF16, MASK>(s1, d1, Ls, Ds, 32 + 8 * h, a.c, lim - 32, pb1, sb1);
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_accum<BF16, D>(Qb, Gb, 1, of, pb1, sb1, dkacc, dvacc);
-    };
+        // One query tile of two 32-row blocks.  The scores of the second block are
+        // issued before the first block's element-wise work, which then runs beside
+        // those matrix instructions.
+        auto step = [&](const unsigned char* st, int i0, auto mask) {
+            constexpr bool MASK = decltype(mask)::value;
+            const unsigned char* Qb = st;
+            const unsigned char* Gb = st + QTILE;
+            const float* Ls = (const float*)(st + 2 * QTILE);
+            const float* Ds = (const float*)(st + 2 * QTILE + 1024);
+            const int lim = kj - i0 - off - 8 * h;
+            f32x16 s0, d0, s1, d1;
+            u32x4 pb[2], sb[2];
+            // scheduling fences keep the compiler to these four phases
+            scores<BF16, D>(Qb, Gb, 0, of, kf, vf, s0, d0);
+            __builtin_amdgcn_sched_barrier(0);
+            scores<BF16, D>(Qb, Gb, 1, of, kf, vf, s1, d1);
+            dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
+            __builtin_amdgcn_sched_barrier(0);
+            dkdv_accum<BF16, D>(Qb, Gb, 0, of, pb, sb, dkacc, dvacc);
+            u32x4 pb1[2], sb1[2];
+            dkdv_probs<BF16, MASK>(s1, d1, Ls, Ds, 32 + 8 * h, a.c, lim - 32, pb1, sb1);
+            __builtin_amdgcn_sched_barrier(0);
+            dkdv_accum<BF16, D>(Qb, Gb, 1, of, pb1, sb1, dkacc, dvacc);
+        };
 
-    // query tiles upward from the diagonal: the first ones may hold rows that do
-    // not yet see some keys of the block
-    if (n_tiles > 0) load_tile(t0, stage0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // two tiles per trip, so that each step reads one fixed LDS stage
-    auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
-        const int tile = t0 + it;
-        if (it + 1 < n_tiles) load_tile(tile + 1, nxt);
-        const int i0 = tile * CQ;
-        // causal: a wave whose keys every row of the tile sees needs no mask, and
-        // one whose keys no row sees yet skips the tile
-        if (!CAUSAL || kw + 31 <= i0 + off) step(cur, i0, std::false_type{});
-        else if (kw <= i0 + CQ - 1 + off) step(cur, i0, std::true_type{});
+        // query tiles upward from the diagonal: the first ones may hold rows that do
+        // not yet see some keys of the block
+        if (n_tiles > 0) load_tile(t0, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-    };
-#pragma clang loop unroll(disable)
-    for (int it = 0; it < n_tiles; it += 2) {
-        one(it, stage0, stage1);
-        if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
-    }
+        // two tiles per trip, so that each step reads one fixed LDS stage
+        auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
+            const int tile = t0 + it;
+            if (it + 1 < n_tiles) load_tile(tile + 1, nxt);
+            const int i0 = tile * CQ;
+            // causal: a wave whose keys every row of the tile sees needs no mask, and
+            // one whose keys no row sees yet skips the tile
+            if (!CAUSAL || kw + 31 <= i0 + off) step(cur, i0, std::false_type{});
+            else if (kw <= i0 + CQ - 1 + off) step(cur, i0, std::true_type{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+    #pragma clang loop unroll(disable)
+        for (int it = 0; it < n_tiles; it += 2) {
+            one(it, stage0, stage1);
+            if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
+        }
 
-    if (kok) {
-        uint16_t* dkp = a.dk + ((size_t)bh * Nk + kj) * D;
-        uint16_t* dvp = a.dv + ((size_t)bh * Nk + kj) * D;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c0 = 32 * db + 8 * g + 4 * h;
-                const u32x2 k2 = {pack2<BF16>(dkacc[db][4 * g] * a.scale, dkacc[db][4 * g + 1] * a.scale),
-                                  pack2<BF16>(dkacc[db][4 * g + 2] * a.scale, dkacc[db][4 * g + 3] * a.scale)};
-                const u32x2 v2 = {pack2<BF16>(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
-                                  pack2<BF16>(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
-                *(u32x2*)(dkp + c0) = k2;
-                *(u32x2*)(dvp + c0) = v2;
-            }
-    }
+        if (kok) {
+            uint16_t* dkp = a.dk + ((size_t)bh * Nk + kj) * D;
+            uint16_t* dvp = a.dv + ((size_t)bh * Nk + kj) * D;
+    #pragma unroll
+            for (int db = 0; db < ND; ++db)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c0 = 32 * db + 8 * g + 4 * h;
+                    const u32x2 k2 = {pack2<BF16>(dkacc[db][4 * g] * a.scale, dkacc[db][4 * g + 1] * a.scale),
+                                      pack2<BF16>(dkacc[db][4 * g + 2] * a.scale, dkacc[db][4 * g + 3] * a.scale)};
+                    const u32x2 v2 = {pack2<BF16>(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
+                                      pack2<BF16>(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
+                    *(u32x2*)(dkp + c0) = k2;
+                    *(u32x2*)(dvp + c0) = v2;
+                }
+        }
+    };
+    for_items<CAUSAL>(a.n_ktiles, a.BH, run_item);
 }
 
 template <bool BF16, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
     const int64_t dblocks = (rows + 255) / 256;
     hipLaunchKernelGGL((bwd_delta_kernel<BF16, D>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
-    const int kv_blocks = a.n_ktiles * a.BH, q_blocks = a.n_qtiles * a.BH;
+    const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH);
+    const int q_blocks = (int)item_blocks(causal, a.n_qtiles, a.BH);
     if (causal) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true>), dim3(kv_blocks), dim3(256), 0, s, a);
         hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true>), dim3(q_blocks), dim3(256), 0, s, a);

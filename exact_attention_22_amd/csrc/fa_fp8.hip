@@ -106,214 +106,227 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
     __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];   // [K | V]
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
-    // work item: XCD-contiguous ranges, heaviest causal query tile first
+    // work items: XCD-contiguous ranges.  Causal: one workgroup runs query tiles
+    // n_qtiles-1-t and t, which together see a fixed number of key tiles (equal
+    // work per workgroup for the round-robin dispatcher); otherwise one tile.
     const int total = gridDim.x;
     int L = blockIdx.x;
     if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-    const int qt = a.n_qtiles - 1 - (L % a.n_qtiles);
-    const int bh = (L / a.n_qtiles) % a.BH;
-    const int bkv = (bh / a.H) * a.H_kv + (bh % a.H) / a.group;
-    const int q0 = qt * F8_BR;
-    const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+    auto run_item = [&](const int qt, const int bh) __attribute__((always_inline)) {
+        const int bkv = (bh / a.H) * a.H_kv + (bh % a.H) / a.group;
+        const int q0 = qt * F8_BR;
+        const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, h = lane >> 5;
-    const int qw = q0 + 32 * w, qi = qw + l32;
+        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l32 = lane & 31, h = lane >> 5;
+        const int qw = q0 + 32 * w, qi = qw + l32;
 
-    const uint8_t* qg = a.q + (size_t)bh * Nq * F8_D;
-    const uint8_t* kg = a.k + (size_t)bkv * Nk * F8_D;
-    const uint8_t* vg = a.v + (size_t)bkv * Nk * F8_D;
-    const float cq = a.c * a.qd[(size_t)bh * a.n_qtiles + qt];
-    const float* kdh = a.kd + (size_t)bkv * a.n_kblk;
+        const uint8_t* qg = a.q + (size_t)bh * Nq * F8_D;
+        const uint8_t* kg = a.k + (size_t)bkv * Nk * F8_D;
+        const uint8_t* vg = a.v + (size_t)bkv * Nk * F8_D;
+        const float cq = a.c * a.qd[(size_t)bh * a.n_qtiles + qt];
+        const float* kdh = a.kd + (size_t)bkv * a.n_kblk;
 
-    int hi = Nk;
-    if (CAUSAL) hi = min(hi, min(Nq, q0 + F8_BR) + off);
-    const int n_tiles = hi > 0 ? (hi + F8_BC - 1) / F8_BC : 0;
+        int hi = Nk;
+        if (CAUSAL) hi = min(hi, min(Nq, q0 + F8_BR) + off);
+        const int n_tiles = hi > 0 ? (hi + F8_BC - 1) / F8_BC : 0;
 
-    // Q: bytes 64ks + 32h .. +31 of this lane's row, for ks = 0, 1
-    i32x8 qf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        if (qi < Nq) {
-            const u32x4* src = (const u32x4*)(qg + (size_t)qi * F8_D + 64 * ks + 32 * h);
-            const u32x4 x0 = src[0], x1 = src[1];
-            qf[ks] = i32x8{(int)(x0[0] ^ a.qsign), (int)(x0[1] ^ a.qsign), (int)(x0[2] ^ a.qsign),
-                           (int)(x0[3] ^ a.qsign), (int)(x1[0] ^ a.qsign), (int)(x1[1] ^ a.qsign),
-                           (int)(x1[2] ^ a.qsign), (int)(x1[3] ^ a.qsign)};
-        } else {
-            qf[ks] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
-
-    // LDS-direct loads: lane i of a 1 KiB load lands at byte 16 i; it fetches the
-    // global chunk that the swizzled layout keeps there
-    u32 voff[NPW];
-#pragma unroll
-    for (int u = 0; u < NPW; ++u) {
-        const int pos = (w * NPW + u) * 1024 + lane * 16;
-        const int row = pos / F8_D, pchunk = (pos % F8_D) >> 4;
-        voff[u] = (u32)(row * F8_D + ((pchunk ^ f8_swz(row)) << 4));
-    }
-    auto load_tile = [&](int tile, unsigned char* stage) {
-        const int k0 = tile * F8_BC;
-        const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(Nk - k0, F8_BC)) * F8_D;
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + (size_t)k0 * F8_D, nrec);
-        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + (size_t)k0 * F8_D, nrec);
-#pragma unroll
-        for (int u = 0; u < NPW; ++u) lds_dma16(rk, stage + (w * NPW + u) * 1024, voff[u]);
-#pragma unroll
-        for (int u = 0; u < NPW; ++u) lds_dma16(rv, stage + TILE + (w * NPW + u) * 1024, voff[u]);
-    };
-
-    // operand offsets: K chunks 4ks + 2h and 4ks + 2h + 1 of row f8_perm_row(l32)
-    // (32-key blocks only add constants); V^T reads as in the file comment
-    const int krow = f8_perm_row(l32);
-    int koff[2][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) koff[ks][j] = f8_off(krow, 4 * ks + 2 * h + j);
-    const int s16 = lane & 15, g16 = lane >> 4;
-    const int vrow = 8 * h + (s16 >> 1);
-    int vo[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) vo[db] = f8_off(vrow, 2 * db + (g16 & 1)) + 8 * (s16 & 1);
-
-    f32x16 oacc[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
-    float Mu = -INFINITY;   // exponent reference, log2 units of scaled scores
-    float lsum = 0.f;       // this lane's half of the lifted row sum, relative to Mu
-
-    // One key tile: S^T = K Q^T (4 blocks of 32 keys), online softmax update,
-    // O^T += V^T P^T (2 groups of 64 keys).  MASKED tiles cross the key tail or
-    // the causal diagonal.
-    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int tile, auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        const int k0 = tile * F8_BC;
-        const float c = cq * kdh[tile];
-        f32x16 sacc[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sacc[kb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 x0 = *(const u32x4*)(Kb + 32 * kb * F8_D + koff[ks][0]);
-                const u32x4 x1 = *(const u32x4*)(Kb + 32 * kb * F8_D + koff[ks][1]);
-                const i32x8 kf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                                  (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-                sacc[kb] = mfma_f8(kf, qf[ks], sacc[kb]);
+        // Q: bytes 64ks + 32h .. +31 of this lane's row, for ks = 0, 1
+        i32x8 qf[2];
+    #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (qi < Nq) {
+                const u32x4* src = (const u32x4*)(qg + (size_t)qi * F8_D + 64 * ks + 32 * h);
+                const u32x4 x0 = src[0], x1 = src[1];
+                qf[ks] = i32x8{(int)(x0[0] ^ a.qsign), (int)(x0[1] ^ a.qsign), (int)(x0[2] ^ a.qsign),
+                               (int)(x0[3] ^ a.qsign), (int)(x1[0] ^ a.qsign), (int)(x1[1] ^ a.qsign),
+                               (int)(x1[2] ^ a.qsign), (int)(x1[3] ^ a.qsign)};
+            } else {
+                qf[ks] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
-        // register r of block kb holds key k0 + 32kb + 16(r/8) + 8h + r%8
-        int bound = 0;
-        if constexpr (MASKED) {
-            bound = Nk - k0 - 8 * h;
-            if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = -INFINITY;
-        }
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[kb][r]);
-        mx = max_halves(mx);
-        const float Mc = (mx == -INFINITY) ? -INFINITY : mx * c;
-        if (__ballot(Mc > Mu + F8_TAU)) {        // wave-uniform: move the reference
-            const float Mn = fmaxf(Mu, Mc);
-            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-            Mu = Mn;
-        }
-        const float bias = F8_LIFT - ((Mu == -INFINITY) ? 0.f : Mu);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = exp2_fast(__builtin_fmaf(sacc[kb][r], c, bias));
-                if constexpr (MASKED)
-                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) p = 0.f;
-                sacc[kb][r] = p;
-                lsum += p;
-            }
-        // O^T += V^T P^T per 64-key group: P bytes in register order, V^T by
-        // transposed reads (read t covers keys 16t + 8h + 0..7 of the group)
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-            const f32x16& P0 = sacc[2 * kg];
-            const f32x16& P1 = sacc[2 * kg + 1];
-            const i32x8 pb = {pack4_f8(P0[0], P0[1], P0[2], P0[3]), pack4_f8(P0[4], P0[5], P0[6], P0[7]),
-                              pack4_f8(P0[8], P0[9], P0[10], P0[11]), pack4_f8(P0[12], P0[13], P0[14], P0[15]),
-                              pack4_f8(P1[0], P1[1], P1[2], P1[3]), pack4_f8(P1[4], P1[5], P1[6], P1[7]),
-                              pack4_f8(P1[8], P1[9], P1[10], P1[11]), pack4_f8(P1[12], P1[13], P1[14], P1[15])};
-#pragma unroll
-            for (int db = 0; db < ND; ++db) {
-                i32x8 va;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) i32x2*)(Vb + (64 * kg + 16 * t) * F8_D + vo[db]));
-                    va[2 * t] = r2[0];
-                    va[2 * t + 1] = r2[1];
-                }
-                oacc[db] = mfma_f8(va, pb, oacc[db]);
-            }
-        }
-    };
 
-    // tiles from the last one down: the ones crossing the key tail or the
-    // diagonal come first
-    int n_masked = 0;
-    while (n_masked < n_tiles) {
-        const int k0 = (n_tiles - 1 - n_masked) * F8_BC;
-        const bool clean = k0 + F8_BC <= Nk && (!CAUSAL || k0 + F8_BC - 1 <= q0 + off);
-        if (clean) break;
-        ++n_masked;
-    }
-    const int qmax_w = min(qw + 31, Nq - 1);
-    if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // two tiles per trip, so that each step reads one fixed LDS stage
-    auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
-        const int tile = n_tiles - 1 - it;
-        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
-        if (it < n_masked) {
+        // LDS-direct loads: lane i of a 1 KiB load lands at byte 16 i; it fetches the
+        // global chunk that the swizzled layout keeps there
+        u32 voff[NPW];
+    #pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int pos = (w * NPW + u) * 1024 + lane * 16;
+            const int row = pos / F8_D, pchunk = (pos % F8_D) >> 4;
+            voff[u] = (u32)(row * F8_D + ((pchunk ^ f8_swz(row)) << 4));
+        }
+        auto load_tile = [&](int tile, unsigned char* stage) {
             const int k0 = tile * F8_BC;
-            if (qw < Nq && (!CAUSAL || k0 <= qmax_w + off)) tile_step(cur, cur + TILE, tile, std::true_type{});
-        } else {
-            tile_step(cur, cur + TILE, tile, std::false_type{});
+            const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(Nk - k0, F8_BC)) * F8_D;
+            const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + (size_t)k0 * F8_D, nrec);
+            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + (size_t)k0 * F8_D, nrec);
+    #pragma unroll
+            for (int u = 0; u < NPW; ++u) lds_dma16(rk, stage + (w * NPW + u) * 1024, voff[u]);
+    #pragma unroll
+            for (int u = 0; u < NPW; ++u) lds_dma16(rv, stage + TILE + (w * NPW + u) * 1024, voff[u]);
+        };
+
+        // operand offsets: K chunks 4ks + 2h and 4ks + 2h + 1 of row f8_perm_row(l32)
+        // (32-key blocks only add constants); V^T reads as in the file comment
+        const int krow = f8_perm_row(l32);
+        int koff[2][2];
+    #pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) koff[ks][j] = f8_off(krow, 4 * ks + 2 * h + j);
+        const int s16 = lane & 15, g16 = lane >> 4;
+        const int vrow = 8 * h + (s16 >> 1);
+        int vo[ND];
+    #pragma unroll
+        for (int db = 0; db < ND; ++db) vo[db] = f8_off(vrow, 2 * db + (g16 & 1)) + 8 * (s16 & 1);
+
+        f32x16 oacc[ND];
+    #pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
+        float Mu = -INFINITY;   // exponent reference, log2 units of scaled scores
+        float lsum = 0.f;       // this lane's half of the lifted row sum, relative to Mu
+
+        // One key tile: S^T = K Q^T (4 blocks of 32 keys), online softmax update,
+        // O^T += V^T P^T (2 groups of 64 keys).  MASKED tiles cross the key tail or
+        // the causal diagonal.
+        auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int tile, auto masked_tag) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            const int k0 = tile * F8_BC;
+            const float c = cq * kdh[tile];
+            f32x16 sacc[4];
+    #pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sacc[kb] = f32x16{};
+    #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const u32x4 x0 = *(const u32x4*)(Kb + 32 * kb * F8_D + koff[ks][0]);
+                    const u32x4 x1 = *(const u32x4*)(Kb + 32 * kb * F8_D + koff[ks][1]);
+                    const i32x8 kf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                      (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                    sacc[kb] = mfma_f8(kf, qf[ks], sacc[kb]);
+                }
+            }
+            // register r of block kb holds key k0 + 32kb + 16(r/8) + 8h + r%8
+            int bound = 0;
+            if constexpr (MASKED) {
+                bound = Nk - k0 - 8 * h;
+                if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
+    #pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = -INFINITY;
+            }
+            float mx = sacc[0][0];
+    #pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[kb][r]);
+            mx = max_halves(mx);
+            const float Mc = (mx == -INFINITY) ? -INFINITY : mx * c;
+            if (__ballot(Mc > Mu + F8_TAU)) {        // wave-uniform: move the reference
+                const float Mn = fmaxf(Mu, Mc);
+                const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
+                lsum *= alpha;
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+                Mu = Mn;
+            }
+            const float bias = F8_LIFT - ((Mu == -INFINITY) ? 0.f : Mu);
+    #pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = exp2_fast(__builtin_fmaf(sacc[kb][r], c, bias));
+                    if constexpr (MASKED)
+                        if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) p = 0.f;
+                    sacc[kb][r] = p;
+                    lsum += p;
+                }
+            // O^T += V^T P^T per 64-key group: P bytes in register order, V^T by
+            // transposed reads (read t covers keys 16t + 8h + 0..7 of the group)
+    #pragma unroll
+            for (int kg = 0; kg < 2; ++kg) {
+                const f32x16& P0 = sacc[2 * kg];
+                const f32x16& P1 = sacc[2 * kg + 1];
+                const i32x8 pb = {pack4_f8(P0[0], P0[1], P0[2], P0[3]), pack4_f8(P0[4], P0[5], P0[6], P0[7]),
+                                  pack4_f8(P0[8], P0[9], P0[10], P0[11]), pack4_f8(P0[12], P0[13], P0[14], P0[15]),
+                                  pack4_f8(P1[0], P1[1], P1[2], P1[3]), pack4_f8(P1[4], P1[5], P1[6], P1[7]),
+                                  pack4_f8(P1[8], P1[9], P1[10], P1[11]), pack4_f8(P1[12], P1[13], P1[14], P1[15])};
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    i32x8 va;
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (__attribute__((address_space(3))) i32x2*)(Vb + (64 * kg + 16 * t) * F8_D + vo[db]));
+                        va[2 * t] = r2[0];
+                        va[2 * t + 1] = r2[1];
+                    }
+                    oacc[db] = mfma_f8(va, pb, oacc[db]);
+                }
+            }
+        };
+
+        // tiles from the last one down: the ones crossing the key tail or the
+        // diagonal come first
+        int n_masked = 0;
+        while (n_masked < n_tiles) {
+            const int k0 = (n_tiles - 1 - n_masked) * F8_BC;
+            const bool clean = k0 + F8_BC <= Nk && (!CAUSAL || k0 + F8_BC - 1 <= q0 + off);
+            if (clean) break;
+            ++n_masked;
         }
+        const int qmax_w = min(qw + 31, Nq - 1);
+        if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-    };
-#pragma clang loop unroll(disable)
-    for (int it = 0; it < n_tiles; it += 2) {
-        one(it, stage0, stage1);
-        if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
-    }
-
-    // epilogue: O = vd * O_acc / l (bf16); LSE = (M + log2 l - LIFT) ln 2
-    const float lt = sum_halves(lsum);
-    const float inv = (lt == 0.f || lt != lt) ? 1.f : a.vd[bkv] / lt;
-    const float lse_v = (lt == 0.f) ? -INFINITY : (Mu + log2f(lt) - F8_LIFT) * kLn2;
-    if (qi < Nq) {
-        uint16_t* op = a.o + ((size_t)bh * Nq + qi) * F8_D;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x2 v2 = {pack2<true>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                                  pack2<true>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
+        // two tiles per trip, so that each step reads one fixed LDS stage
+        auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
+            const int tile = n_tiles - 1 - it;
+            if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+            if (it < n_masked) {
+                const int k0 = tile * F8_BC;
+                if (qw < Nq && (!CAUSAL || k0 <= qmax_w + off)) tile_step(cur, cur + TILE, tile, std::true_type{});
+            } else {
+                tile_step(cur, cur + TILE, tile, std::false_type{});
             }
-        if (h == 0) a.lse[(size_t)bh * Nq + qi] = lse_v;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+    #pragma clang loop unroll(disable)
+        for (int it = 0; it < n_tiles; it += 2) {
+            one(it, stage0, stage1);
+            if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
+        }
+
+        // epilogue: O = vd * O_acc / l (bf16); LSE = (M + log2 l - LIFT) ln 2
+        const float lt = sum_halves(lsum);
+        const float inv = (lt == 0.f || lt != lt) ? 1.f : a.vd[bkv] / lt;
+        const float lse_v = (lt == 0.f) ? -INFINITY : (Mu + log2f(lt) - F8_LIFT) * kLn2;
+        if (qi < Nq) {
+            uint16_t* op = a.o + ((size_t)bh * Nq + qi) * F8_D;
+    #pragma unroll
+            for (int db = 0; db < ND; ++db)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2 v2 = {pack2<true>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                      pack2<true>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
+                }
+            if (h == 0) a.lse[(size_t)bh * Nq + qi] = lse_v;
+        }
+    };
+    if (CAUSAL && a.n_qtiles >= 2) {
+        const int npairs = (a.n_qtiles + 1) >> 1;
+        const int t = L % npairs, bh = L / npairs;
+        run_item(a.n_qtiles - 1 - t, bh);
+        if (t != a.n_qtiles - 1 - t) {
+            __syncthreads();        // the next item refills stage0
+            run_item(t, bh);
+        }
+    } else {
+        run_item(a.n_qtiles - 1 - (L % a.n_qtiles), (L / a.n_qtiles) % a.BH);
     }
 }
 
@@ -382,7 +395,8 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream) {
     a.n_kblk = (p.Nk + F8_BC - 1) / F8_BC;
     a.c = fabsf(p.scale) * kLog2e;
     a.qsign = p.scale < 0.f ? 0x80808080u : 0u;
-    const int64_t blocks = (int64_t)a.n_qtiles * a.BH;
+    const int64_t blocks = (p.causal && a.n_qtiles >= 2) ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH
+                                                         : (int64_t)a.n_qtiles * a.BH;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.causal)
         hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3((int)blocks), dim3(256), 0, stream, a);

@@ -42,8 +42,12 @@
 //     probability, decided per wavefront.  Any reference gives the same
 //     O = sum 2^(t-M) v / sum 2^(t-M); keeping the reference at or below the
 //     true maximum keeps every P <= 256, well inside fp16 range.
-//   * Workgroups are ordered heaviest causal tile first and mapped so that
-//     consecutive tiles of one head share an XCD (and its L2).
+//   * Workgroups are mapped so that consecutive tiles of one head share an XCD
+//     (and its L2).  Causal [B, H, N, d]: one workgroup runs query tiles
+//     n_qtiles-1-t and t, which together see a fixed number of key tiles, so
+//     every workgroup carries the same work and the XCD round-robin dispatcher
+//     never stalls on one XCD's long tile; otherwise (and for packed sequences)
+//     the heaviest tile goes first.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -75,6 +79,7 @@ struct FwdArgs {
     const int* cu_k;
     int H_kv, group;   // group = H / H_kv query heads per K/V head
     int total_q, total_k, max_q, max_k;
+    int paired;        // causal [B,H,N,d]: one workgroup runs query tiles n_qtiles-1-t and t
 };
 
 // Key index (within a 32-key block) that accumulator row i stands for: bits 2 and 3 swapped.
@@ -94,10 +99,292 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
-    // ---- work item -------------------------------------------------------
+    // ---- work items ------------------------------------------------------
     // Workgroup b runs on XCD b % 8 (the hardware dispatches round-robin).
     const int total = gridDim.x;
-    int qt, bh, split = 0;
+    int L = blockIdx.x;
+    if (!VARLEN && (total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);   // XCD-contiguous ranges
+    // One query tile of one (sequence, head[, split]).
+    auto run_item = [&](const int qt, const int bh, const int split) __attribute__((always_inline)) {
+        const int q0 = qt * BR;
+
+        // ---- this item's sequence: sizes, base pointers, row strides -------------
+        int Nq = a.Nq, Nk = a.Nk;
+        const uint16_t* qg;                           // row 0 of this (sequence, head)
+        const uint16_t* kg;
+        const uint16_t* vg;
+        int q_rs = D, kv_rs = D;                      // elements between consecutive rows
+        size_t o0 = (size_t)bh * a.Nq * D;            // element offset of this item's output row 0
+        int o_rs = D;
+        float* lse_g = a.lse + (size_t)bh * a.Nq;
+        if constexpr (VARLEN) {
+            // Offsets come from the caller's device arrays: a sequence whose offsets
+            // leave [0, total], decrease or exceed the declared maximum is skipped,
+            // so no access ever leaves the tensors.
+            const int b = bh / a.H, hq = bh - b * a.H;
+            const int qs = a.cu_q[b], qe = a.cu_q[b + 1], ks0 = a.cu_k[b], ke0 = a.cu_k[b + 1];
+            if (qs < 0 || qe < qs || qe > a.total_q || qe - qs > a.max_q) return;
+            if (ks0 < 0 || ke0 < ks0 || ke0 > a.total_k || ke0 - ks0 > a.max_k) return;
+            Nq = qe - qs;
+            Nk = ke0 - ks0;
+            if (q0 >= Nq) return;
+            const int hk = hq / a.group;
+            q_rs = a.H * D;
+            kv_rs = a.H_kv * D;
+            o_rs = a.H * D;
+            qg = a.q + (size_t)qs * q_rs + (size_t)hq * D;
+            kg = a.k + (size_t)ks0 * kv_rs + (size_t)hk * D;
+            vg = a.v + (size_t)ks0 * kv_rs + (size_t)hk * D;
+            o0 = (size_t)qs * o_rs + (size_t)hq * D;
+            lse_g = a.lse + (size_t)hq * a.total_q + qs;
+        } else {
+            // [B, H, N, d] queries; keys and values [B, H_kv, N, d], query head h
+            // reading K/V head h / group (group = 1 without grouped heads)
+            const int bkv = a.group == 1 ? bh : (bh / a.H) * a.H_kv + (bh % a.H) / a.group;
+            qg = a.q + (size_t)bh * a.Nq * D;
+            kg = a.k + (size_t)bkv * a.Nk * D;
+            vg = a.v + (size_t)bkv * a.Nk * D;
+        }
+        const int kv_rowb = kv_rs * 2;                // bytes between consecutive K/V rows
+
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
+        const int l32 = lane & 31;
+        const int h = lane >> 5;
+        const int qw = q0 + 32 * w;
+        const int qi = qw + l32;
+        const int off = Nk - Nq;                      // causal: key j visible iff j <= i + off
+
+        int ks = 0, ke = Nk;
+        if (SPLIT) {
+            ks = min(Nk, split * a.split_chunk);
+            ke = min(Nk, ks + a.split_chunk);
+        }
+        int hi = ke;
+        if (CAUSAL) hi = min(hi, min(Nq, q0 + BR) - 1 + off + 1);
+        const int n_tiles = hi > ks ? (hi - ks + BC - 1) / BC : 0;
+
+        // ---- Q fragments, resident for the whole key loop ----------------------
+        u32x4 qf[NS];
+    #pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (qi < Nq) {
+                qf[s] = *(const u32x4*)(qg + (size_t)qi * q_rs + 16 * s + 8 * h);
+                qf[s] ^= a.qsign;
+            } else {
+                qf[s] = u32x4{0, 0, 0, 0};
+            }
+        }
+
+        // ---- K/V tiles: buffer loads straight into LDS ---------------------------
+        // One wave instruction fills 1 KiB of LDS, lane i landing at byte 16*i.  Lane
+        // i therefore fetches the global chunk that the swizzled layout stores at
+        // that position (global rows are kv_rowb bytes apart); these offsets do not
+        // change from tile to tile.  Reads past the sequence's last key return zeros
+        // (the descriptor's record count ends with that key's row).
+        constexpr int NPW = TILE / 1024 / 4;         // 1 KiB loads per wave per tensor per tile
+        u32 voff[NPW];
+    #pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int pos = (w * NPW + u) * 1024 + lane * 16;
+            const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
+            voff[u] = (u32)(row * kv_rowb + ((pchunk ^ swz<D>(row)) << 4));
+        }
+        // which = 0 loads the K tile of `tile` into the stage, 1 its V tile
+        auto load_half = [&](int tile, unsigned char* stage, int which) {
+            const int k0 = ks + tile * BC;
+            const u32 nrec = (u32)(min(Nk - k0, BC) - 1) * kv_rowb + ROWB;
+            const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * kv_rs, nrec);
+            unsigned char* dst = stage + which * TILE + w * NPW * 1024;
+    #pragma unroll
+            for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
+        };
+        auto load_tile = [&](int tile, unsigned char* stage) {
+            load_half(tile, stage, 0);
+            load_half(tile, stage, 1);
+        };
+
+        f32x16 oacc[ND];
+    #pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
+        float Mu = -INFINITY;   // exponent reference (log2 units of scaled scores)
+        float lsum = 0.f;       // this lane's half of the row sum, relative to Mu
+
+        // per-lane LDS byte offsets of the operand reads (rows differing in bits
+        // 4-5 share a swizzle, so the 32-key block and 16-key group only add constants)
+        const int krow0 = perm_row(l32);             // K row fed to S^T within a 32-key block
+        int koff[NS];
+    #pragma unroll
+        for (int s = 0; s < NS; ++s) koff[s] = lds_off<D>(krow0, 2 * s + h);
+        const int r4 = (lane & 15) >> 2, c4 = lane & 3, g1 = (lane >> 4) & 1;
+        int voffs[2][ND];
+    #pragma unroll
+        for (int half = 0; half < 2; ++half)
+    #pragma unroll
+            for (int db = 0; db < ND; ++db)
+                voffs[half][db] = lds_off<D>(8 * h + r4 + 4 * half, 4 * db + 2 * g1 + (c4 >> 1)) + (c4 & 1) * 8;
+
+        // One key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
+        // MASKED tiles cross the chunk end or (causal) the diagonal.  after_s runs
+        // once the S^T products are issued.
+        auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag,
+                             auto&& after_s) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            f32x16 sacc[2];
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                sacc[kb] = f32x16{};
+    #pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const u32x4 kf = *(const u32x4*)(Kb + 32 * kb * ROWB + koff[s]);
+                    sacc[kb] = mfma32<BF16>(kf, qf[s], sacc[kb]);
+                }
+            }
+            after_s();
+            // register r of block kb holds key k0 + 8h + kofs(kb, r); visible iff kofs < bound
+            int bound = 0;
+            if constexpr (MASKED) {
+                bound = ke - k0 - 8 * h;
+                if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = -INFINITY;
+            }
+            // row max over this tile (raw scores), both lane halves
+            float mx = sacc[0][0];
+    #pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sacc[0][r]);
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[1][r]);
+            mx = max_halves(mx);
+            const float Mc = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+            if (__ballot(Mc > Mu + TAU)) {          // wave-uniform: move the reference
+                const float Mn = fmaxf(Mu, Mc);
+                const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
+                lsum *= alpha;
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+                Mu = Mn;
+            }
+            const float Mg = (Mu == -INFINITY) ? 0.f : Mu;   // no -inf - -inf
+            // P = 2^(s*c - M); masked keys weigh exactly 0 (also when scale is 0)
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
+                    if constexpr (MASKED)
+                        if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) p = 0.f;
+                    sacc[kb][r] = p;
+                }
+            // row sum in fp32, before P is rounded to 16 bits
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) lsum += sacc[kb][r];
+            // O^T += V^T P^T
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const f32x16& P = sacc[kb];
+                    const u32x4 pb = {pack2<BF16>(P[8 * p + 0], P[8 * p + 1]), pack2<BF16>(P[8 * p + 2], P[8 * p + 3]),
+                                      pack2<BF16>(P[8 * p + 4], P[8 * p + 5]), pack2<BF16>(P[8 * p + 6], P[8 * p + 7])};
+                    const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
+    #pragma unroll
+                    for (int db = 0; db < ND; ++db) {
+                        const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
+                        const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
+                        const u32x4 va = {l2[0], l2[1], h2[0], h2[1]};
+                        oacc[db] = mfma32<BF16>(va, pb, oacc[db]);
+                    }
+                }
+        };
+
+        // Tiles are walked from the last one down.  The first n_masked of them may
+        // cross the key-chunk end or the causal diagonal for some wave; all later
+        // ones are fully visible to every row of the workgroup.
+        int n_masked = 0;
+        while (n_masked < n_tiles) {
+            const int k0 = ks + (n_tiles - 1 - n_masked) * BC;
+            const bool clean = k0 + BC <= ke && (!CAUSAL || k0 + BC - 1 <= q0 + off);
+            if (clean) break;
+            ++n_masked;
+        }
+        const int qmax_w = min(qw + 31, Nq - 1);
+        if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // masked tiles: per-wave visibility checks, stage chosen at run time
+        int it = 0;
+    #pragma clang loop unroll(disable)
+        for (; it < n_masked; ++it) {
+            const int tile = n_tiles - 1 - it;
+            unsigned char* cur = (it & 1) ? stage1 : stage0;
+            unsigned char* nxt = (it & 1) ? stage0 : stage1;
+            if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+            const int k0 = ks + tile * BC;
+            const bool active = qw < Nq && (!CAUSAL || k0 <= qmax_w + off);
+            if (active) tile_step(cur, cur + TILE, k0, std::true_type{}, [] {});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        // clean tiles, two per trip so that each half reads one fixed stage.  The
+        // next tile's K loads go out at the start of the step and its V loads after
+        // the S^T products: one burst of all of a workgroup's loads would queue in
+        // the CU's address unit and stall every wave at the step start.
+        auto clean_step = [&](unsigned char* cur, unsigned char* nxt) {
+            const int tile = n_tiles - 1 - it;
+            const bool more = it + 1 < n_tiles;
+            if (more) load_half(tile - 1, nxt, 0);
+            tile_step(cur, cur + TILE, ks + tile * BC, std::false_type{}, [&] {
+                if (more) load_half(tile - 1, nxt, 1);
+            });
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            ++it;
+        };
+        if ((it & 1) && it < n_tiles) clean_step(stage1, stage0);
+    #pragma clang loop unroll(disable)
+        while (it < n_tiles) {
+            clean_step(stage0, stage1);
+            if (it < n_tiles) clean_step(stage1, stage0);
+        }
+
+        // ---- epilogue -------------------------------------------------------------
+        const float lt = sum_halves(lsum);
+        const float inv = (lt == 0.f || lt != lt) ? 1.f : 1.f / lt;
+        const float lse_v = (lt == 0.f) ? -INFINITY : (Mu + log2f(lt)) * kLn2;
+        if (qi < Nq) {
+            if constexpr (SPLIT) {
+                float* op = (float*)a.o + (((size_t)split * a.BH + bh) * a.Nq + qi) * D;
+    #pragma unroll
+                for (int db = 0; db < ND; ++db)
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v4 = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                          oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+                        *(f32x4*)(op + 32 * db + 8 * g + 4 * h) = v4;
+                    }
+                if (h == 0) a.lse[((size_t)split * a.BH + bh) * a.Nq + qi] = lse_v;
+            } else {
+                uint16_t* op = (uint16_t*)a.o + o0 + (size_t)qi * o_rs;
+    #pragma unroll
+                for (int db = 0; db < ND; ++db)
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const u32x2 v2 = {pack2<BF16>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                          pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                        *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
+                    }
+                if (h == 0) lse_g[qi] = lse_v;
+            }
+        }
+    };
+
     if (VARLEN && ((a.B * a.H_kv) & 7) == 0) {
         // Packed sequences differ in length, so contiguous ranges would leave one
         // XCD with the longest sequence: instead K/V group (b, hk) goes to XCD
@@ -106,292 +393,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int j = blockIdx.x >> 3, gi = j / per_group, r = j - gi * per_group;
         const int grp = gi * 8 + (blockIdx.x & 7);
         const int b = grp / a.H_kv, hk = grp - b * a.H_kv;
-        qt = a.n_qtiles - 1 - r / a.group;                        // heaviest first
-        bh = b * a.H + hk * a.group + r % a.group;
+        run_item(a.n_qtiles - 1 - r / a.group, b * a.H + hk * a.group + r % a.group, 0);   // heaviest first
+    } else if (CAUSAL && !VARLEN && !SPLIT && a.paired) {
+        // Causal query tiles t and n_qtiles-1-t together see a fixed number of key
+        // tiles, so pairing them gives every workgroup the same work: the
+        // round-robin dispatcher then never waits on one XCD's long tile while
+        // another XCD has free slots.
+        const int npairs = (a.n_qtiles + 1) >> 1;
+        const int t = L % npairs, bh = L / npairs;
+        run_item(a.n_qtiles - 1 - t, bh, 0);
+        if (t != a.n_qtiles - 1 - t) {
+            __syncthreads();        // the next item refills stage0
+            run_item(t, bh, 0);
+        }
     } else {
-        int L = blockIdx.x;
-        if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);   // XCD-contiguous ranges
-        qt = a.n_qtiles - 1 - (L % a.n_qtiles);                   // heaviest first
         const int rest = L / a.n_qtiles;
-        bh = rest % a.BH;
-        if (SPLIT) split = rest / a.BH;
-    }
-    const int q0 = qt * BR;
-
-    // ---- this item's sequence: sizes, base pointers, row strides -------------
-    int Nq = a.Nq, Nk = a.Nk;
-    const uint16_t* qg;                           // row 0 of this (sequence, head)
-    const uint16_t* kg;
-    const uint16_t* vg;
-    int q_rs = D, kv_rs = D;                      // elements between consecutive rows
-    size_t o0 = (size_t)bh * a.Nq * D;            // element offset of this item's output row 0
-    int o_rs = D;
-    float* lse_g = a.lse + (size_t)bh * a.Nq;
-    if constexpr (VARLEN) {
-        // Offsets come from the caller's device arrays: a sequence whose offsets
-        // leave [0, total], decrease or exceed the declared maximum is skipped,
-        // so no access ever leaves the tensors.
-        const int b = bh / a.H, hq = bh - b * a.H;
-        const int qs = a.cu_q[b], qe = a.cu_q[b + 1], ks0 = a.cu_k[b], ke0 = a.cu_k[b + 1];
-        if (qs < 0 || qe < qs || qe > a.total_q || qe - qs > a.max_q) return;
-        if (ks0 < 0 || ke0 < ks0 || ke0 > a.total_k || ke0 - ks0 > a.max_k) return;
-        Nq = qe - qs;
-        Nk = ke0 - ks0;
-        if (q0 >= Nq) return;
-        const int hk = hq / a.group;
-        q_rs = a.H * D;
-        kv_rs = a.H_kv * D;
-        o_rs = a.H * D;
-        qg = a.q + (size_t)qs * q_rs + (size_t)hq * D;
-        kg = a.k + (size_t)ks0 * kv_rs + (size_t)hk * D;
-        vg = a.v + (size_t)ks0 * kv_rs + (size_t)hk * D;
-        o0 = (size_t)qs * o_rs + (size_t)hq * D;
-        lse_g = a.lse + (size_t)hq * a.total_q + qs;
-    } else {
-        // [B, H, N, d] queries; keys and values [B, H_kv, N, d], query head h
-        // reading K/V head h / group (group = 1 without grouped heads)
-        const int bkv = a.group == 1 ? bh : (bh / a.H) * a.H_kv + (bh % a.H) / a.group;
-        qg = a.q + (size_t)bh * a.Nq * D;
-        kg = a.k + (size_t)bkv * a.Nk * D;
-        vg = a.v + (size_t)bkv * a.Nk * D;
-    }
-    const int kv_rowb = kv_rs * 2;                // bytes between consecutive K/V rows
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
-    const int l32 = lane & 31;
-    const int h = lane >> 5;
-    const int qw = q0 + 32 * w;
-    const int qi = qw + l32;
-    const int off = Nk - Nq;                      // causal: key j visible iff j <= i + off
-
-    int ks = 0, ke = Nk;
-    if (SPLIT) {
-        ks = min(Nk, split * a.split_chunk);
-        ke = min(Nk, ks + a.split_chunk);
-    }
-    int hi = ke;
-    if (CAUSAL) hi = min(hi, min(Nq, q0 + BR) - 1 + off + 1);
-    const int n_tiles = hi > ks ? (hi - ks + BC - 1) / BC : 0;
-
-    // ---- Q fragments, resident for the whole key loop ----------------------
-    u32x4 qf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (qi < Nq) {
-            qf[s] = *(const u32x4*)(qg + (size_t)qi * q_rs + 16 * s + 8 * h);
-            qf[s] ^= a.qsign;
-        } else {
-            qf[s] = u32x4{0, 0, 0, 0};
-        }
-    }
-
-    // ---- K/V tiles: buffer loads straight into LDS ---------------------------
-    // One wave instruction fills 1 KiB of LDS, lane i landing at byte 16*i.  Lane
-    // i therefore fetches the global chunk that the swizzled layout stores at
-    // that position (global rows are kv_rowb bytes apart); these offsets do not
-    // change from tile to tile.  Reads past the sequence's last key return zeros
-    // (the descriptor's record count ends with that key's row).
-    constexpr int NPW = TILE / 1024 / 4;         // 1 KiB loads per wave per tensor per tile
-    u32 voff[NPW];
-#pragma unroll
-    for (int u = 0; u < NPW; ++u) {
-        const int pos = (w * NPW + u) * 1024 + lane * 16;
-        const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
-        voff[u] = (u32)(row * kv_rowb + ((pchunk ^ swz<D>(row)) << 4));
-    }
-    // which = 0 loads the K tile of `tile` into the stage, 1 its V tile
-    auto load_half = [&](int tile, unsigned char* stage, int which) {
-        const int k0 = ks + tile * BC;
-        const u32 nrec = (u32)(min(Nk - k0, BC) - 1) * kv_rowb + ROWB;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * kv_rs, nrec);
-        unsigned char* dst = stage + which * TILE + w * NPW * 1024;
-#pragma unroll
-        for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
-    };
-    auto load_tile = [&](int tile, unsigned char* stage) {
-        load_half(tile, stage, 0);
-        load_half(tile, stage, 1);
-    };
-
-    f32x16 oacc[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
-    float Mu = -INFINITY;   // exponent reference (log2 units of scaled scores)
-    float lsum = 0.f;       // this lane's half of the row sum, relative to Mu
-
-    // per-lane LDS byte offsets of the operand reads (rows differing in bits
-    // 4-5 share a swizzle, so the 32-key block and 16-key group only add constants)
-    const int krow0 = perm_row(l32);             // K row fed to S^T within a 32-key block
-    int koff[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) koff[s] = lds_off<D>(krow0, 2 * s + h);
-    const int r4 = (lane & 15) >> 2, c4 = lane & 3, g1 = (lane >> 4) & 1;
-    int voffs[2][ND];
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-            voffs[half][db] = lds_off<D>(8 * h + r4 + 4 * half, 4 * db + 2 * g1 + (c4 >> 1)) + (c4 & 1) * 8;
-
-    // One key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
-    // MASKED tiles cross the chunk end or (causal) the diagonal.  after_s runs
-    // once the S^T products are issued.
-    auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag,
-                         auto&& after_s) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = f32x16{};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const u32x4 kf = *(const u32x4*)(Kb + 32 * kb * ROWB + koff[s]);
-                sacc[kb] = mfma32<BF16>(kf, qf[s], sacc[kb]);
-            }
-        }
-        after_s();
-        // register r of block kb holds key k0 + 8h + kofs(kb, r); visible iff kofs < bound
-        int bound = 0;
-        if constexpr (MASKED) {
-            bound = ke - k0 - 8 * h;
-            if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = -INFINITY;
-        }
-        // row max over this tile (raw scores), both lane halves
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sacc[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[1][r]);
-        mx = max_halves(mx);
-        const float Mc = (mx == -INFINITY) ? -INFINITY : mx * a.c;
-        if (__ballot(Mc > Mu + TAU)) {          // wave-uniform: move the reference
-            const float Mn = fmaxf(Mu, Mc);
-            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-            Mu = Mn;
-        }
-        const float Mg = (Mu == -INFINITY) ? 0.f : Mu;   // no -inf - -inf
-        // P = 2^(s*c - M); masked keys weigh exactly 0 (also when scale is 0)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
-                if constexpr (MASKED)
-                    if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) p = 0.f;
-                sacc[kb][r] = p;
-            }
-        // row sum in fp32, before P is rounded to 16 bits
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) lsum += sacc[kb][r];
-        // O^T += V^T P^T
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const f32x16& P = sacc[kb];
-                const u32x4 pb = {pack2<BF16>(P[8 * p + 0], P[8 * p + 1]), pack2<BF16>(P[8 * p + 2], P[8 * p + 3]),
-                                  pack2<BF16>(P[8 * p + 4], P[8 * p + 5]), pack2<BF16>(P[8 * p + 6], P[8 * p + 7])};
-                const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) {
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
-                    const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
-                    const u32x4 va = {l2[0], l2[1], h2[0], h2[1]};
-                    oacc[db] = mfma32<BF16>(va, pb, oacc[db]);
-                }
-            }
-    };
-
-    // Tiles are walked from the last one down.  The first n_masked of them may
-    // cross the key-chunk end or the causal diagonal for some wave; all later
-    // ones are fully visible to every row of the workgroup.
-    int n_masked = 0;
-    while (n_masked < n_tiles) {
-        const int k0 = ks + (n_tiles - 1 - n_masked) * BC;
-        const bool clean = k0 + BC <= ke && (!CAUSAL || k0 + BC - 1 <= q0 + off);
-        if (clean) break;
-        ++n_masked;
-    }
-    const int qmax_w = min(qw + 31, Nq - 1);
-    if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // masked tiles: per-wave visibility checks, stage chosen at run time
-    int it = 0;
-#pragma clang loop unroll(disable)
-    for (; it < n_masked; ++it) {
-        const int tile = n_tiles - 1 - it;
-        unsigned char* cur = (it & 1) ? stage1 : stage0;
-        unsigned char* nxt = (it & 1) ? stage0 : stage1;
-        if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
-        const int k0 = ks + tile * BC;
-        const bool active = qw < Nq && (!CAUSAL || k0 <= qmax_w + off);
-        if (active) tile_step(cur, cur + TILE, k0, std::true_type{}, [] {});
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-    // clean tiles, two per trip so that each half reads one fixed stage.  The
-    // next tile's K loads go out at the start of the step and its V loads after
-    // the S^T products: one burst of all of a workgroup's loads would queue in
-    // the CU's address unit and stall every wave at the step start.
-    auto clean_step = [&](unsigned char* cur, unsigned char* nxt) {
-        const int tile = n_tiles - 1 - it;
-        const bool more = it + 1 < n_tiles;
-        if (more) load_half(tile - 1, nxt, 0);
-        tile_step(cur, cur + TILE, ks + tile * BC, std::false_type{}, [&] {
-            if (more) load_half(tile - 1, nxt, 1);
-        });
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        ++it;
-    };
-    if ((it & 1) && it < n_tiles) clean_step(stage1, stage0);
-#pragma clang loop unroll(disable)
-    while (it < n_tiles) {
-        clean_step(stage0, stage1);
-        if (it < n_tiles) clean_step(stage1, stage0);
-    }
-
-    // ---- epilogue -------------------------------------------------------------
-    const float lt = sum_halves(lsum);
-    const float inv = (lt == 0.f || lt != lt) ? 1.f : 1.f / lt;
-    const float lse_v = (lt == 0.f) ? -INFINITY : (Mu + log2f(lt)) * kLn2;
-    if (qi < Nq) {
-        if constexpr (SPLIT) {
-            float* op = (float*)a.o + (((size_t)split * a.BH + bh) * a.Nq + qi) * D;
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 v4 = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                                      oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-                    *(f32x4*)(op + 32 * db + 8 * g + 4 * h) = v4;
-                }
-            if (h == 0) a.lse[((size_t)split * a.BH + bh) * a.Nq + qi] = lse_v;
-        } else {
-            uint16_t* op = (uint16_t*)a.o + o0 + (size_t)qi * o_rs;
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x2 v2 = {pack2<BF16>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                                      pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                    *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
-                }
-            if (h == 0) lse_g[qi] = lse_v;
-        }
+        run_item(a.n_qtiles - 1 - (L % a.n_qtiles), rest % a.BH, SPLIT ? rest / a.BH : 0);   // heaviest first
     }
 }
 
@@ -443,7 +460,10 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     a.max_q = p.Nq;
     a.max_k = p.Nk;
     const int mode = p.varlen ? 2 : (split ? 1 : 0);
-    const int64_t blocks = (int64_t)a.n_qtiles * a.BH * S;
+    // causal [B,H,N,d]: one workgroup per pair of query tiles (two pairs per
+    // workgroup, one dispatch round with no rebalancing, measured slower)
+    a.paired = p.causal && mode == 0 && a.n_qtiles >= 2;
+    const int64_t blocks = a.paired ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH : (int64_t)a.n_qtiles * a.BH * S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.d == 128)
         return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, mode, stream)
