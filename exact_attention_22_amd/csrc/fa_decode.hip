@@ -247,29 +247,66 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     }
 }
 
-template <bool BF16>
+// Max / sum over the 64 lanes of a wavefront (xor butterfly; every lane ends
+// with the result, combined in the same fixed order on every run).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// One wavefront per output row.  Lane l reads the LSE of split l (64 splits per
+// pass), so the row's weights come from one round of loads instead of S
+// dependent ones; the weighted partial rows are then summed in split order.
+template <bool BF16, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ op, const float* __restrict__ lp,
                                                       uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                      int64_t R, int S, int D) {
+                                                      int64_t R, int S) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= R) return;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(size_t)s * R + row]);
-    const int nd = D / 64;   // values per lane (1 or 2)
+    for (int s0 = 0; s0 < S; s0 += 64)
+        if (s0 + lane < S) M = fmaxf(M, lp[(size_t)(s0 + lane) * R + row]);
+    M = wave_max(M);
+    constexpr int nd = D / 64;   // values per lane (1 or 2)
     float num[2] = {0.f, 0.f};
     float den = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float ls = lp[(size_t)s * R + row];
-            if (ls == -INFINITY) continue;
-            const float wgt = exp2_fast((ls - M) * kLog2e);
-            den += wgt;
-            const float* src = op + ((size_t)s * R + row) * D;
-            for (int j = 0; j < nd; ++j) num[j] = __builtin_fmaf(wgt, src[lane + 64 * j], num[j]);
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const float ls = (s0 + lane < S) ? lp[(size_t)(s0 + lane) * R + row] : -INFINITY;
+            const float wl = (ls == -INFINITY) ? 0.f : exp2_fast((ls - M) * kLog2e);
+            den += wl;
+            const int ns = min(64, S - s0);
+            // eight splits per round so their loads are in flight together
+            for (int j0 = 0; j0 < ns; j0 += 8) {
+                float x[8][nd];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = min(j0 + u, ns - 1);
+                    const float* src = op + ((size_t)(s0 + j) * R + row) * D;
+#pragma unroll
+                    for (int c = 0; c < nd; ++c) x[u][c] = src[lane + 64 * c];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float wj = (j0 + u < ns) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0 + u))
+                                                   : 0.f;
+#pragma unroll
+                    for (int c = 0; c < nd; ++c)   // empty splits add nothing
+                        num[c] = (wj != 0.f) ? __builtin_fmaf(wj, x[u][c], num[c]) : num[c];
+                }
+            }
         }
+        den = wave_sum(den);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
     for (int j = 0; j < nd; ++j) {
         const float x = num[j] * inv;
         uint16_t bits;
@@ -335,12 +372,18 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, f
                           int64_t rows, int d, int num_splits, bool bf16, hipStream_t stream) {
     const int64_t blocks = (rows + 3) / 4;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (bf16)
-        hipLaunchKernelGGL((combine_kernel<true>), dim3((int)blocks), dim3(256), 0, stream, o_part, lse_part,
-                           (uint16_t*)o, lse, rows, num_splits, d);
-    else
-        hipLaunchKernelGGL((combine_kernel<false>), dim3((int)blocks), dim3(256), 0, stream, o_part, lse_part,
-                           (uint16_t*)o, lse, rows, num_splits, d);
+    uint16_t* ob = (uint16_t*)o;
+    if (d == 128) {
+        if (bf16) hipLaunchKernelGGL((combine_kernel<true, 128>), dim3((int)blocks), dim3(256), 0, stream, o_part,
+                                     lse_part, ob, lse, rows, num_splits);
+        else hipLaunchKernelGGL((combine_kernel<false, 128>), dim3((int)blocks), dim3(256), 0, stream, o_part,
+                                lse_part, ob, lse, rows, num_splits);
+    } else {
+        if (bf16) hipLaunchKernelGGL((combine_kernel<true, 64>), dim3((int)blocks), dim3(256), 0, stream, o_part,
+                                     lse_part, ob, lse, rows, num_splits);
+        else hipLaunchKernelGGL((combine_kernel<false, 64>), dim3((int)blocks), dim3(256), 0, stream, o_part,
+                                lse_part, ob, lse, rows, num_splits);
+    }
     return hipGetLastError();
 }
 

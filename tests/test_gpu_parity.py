@@ -166,9 +166,14 @@ def test_splitkv(dev, oracle_lib, case, S):
 
 @pytest.mark.parametrize("empty_every", [0, 3, 1])
 @pytest.mark.parametrize("d,dt", [(64, F16), (128, BF16)])
-def test_combine_alone(dev, oracle_lib, empty_every, d, dt):
-    S, B, H, Nq = 5, 2, 3, 7
+@pytest.mark.parametrize("S", [5, 64, 67, 130])
+def test_combine_alone(dev, oracle_lib, empty_every, d, dt, S):
+    """Split counts below, at and past the 64 splits the combine weighs per pass
+    and not a multiple of the 8 it loads per round; an empty split's partial row
+    holds NaN, which must not reach the result (its weight is zero)."""
+    B, H, Nq = 2, 3, 7
     op, lp = make_partials(S, B, H, Nq, d, seed=31, empty_every=empty_every)
+    op[torch.isinf(lp)] = float("nan")
     say(f"fa_splitkv_combine partials S={S} d={d} empty_every={empty_every}")
     o, lse = fa.splitkv_combine(op.to(dev), lp.to(dev), dt)
     torch.cuda.synchronize()
