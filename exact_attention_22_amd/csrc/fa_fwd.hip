@@ -79,7 +79,7 @@ struct FwdArgs {
     const int* cu_k;
     int H_kv, group;   // group = H / H_kv query heads per K/V head
     int total_q, total_k, max_q, max_k;
-    int paired;        // causal [B,H,N,d]: one workgroup runs query tiles n_qtiles-1-t and t
+    int paired;        // one workgroup runs query tiles n-1-t and t (causal [B,H,N,d]; packed sequences)
 };
 
 // Key index (within a 32-key block) that accumulator row i stands for: bits 2 and 3 swapped.
@@ -385,15 +385,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
     };
 
-    if (VARLEN && ((a.B * a.H_kv) & 7) == 0) {
+    if (VARLEN && a.paired) {
         // Packed sequences differ in length, so contiguous ranges would leave one
         // XCD with the longest sequence: instead K/V group (b, hk) goes to XCD
-        // (b*H_kv + hk) % 8, where its H/H_kv query heads share the L2.
-        const int per_group = a.group * a.n_qtiles;
+        // (b*H_kv + hk) % 8, where its H/H_kv query heads share the L2.  Within a
+        // sequence of nb query tiles a workgroup runs tiles nb-1-t and t (equal
+        // work per workgroup of a sequence under the causal mask; half as many
+        // workgroups past the end of short sequences).
+        const int per_group = a.group * ((a.n_qtiles + 1) >> 1);
         const int j = blockIdx.x >> 3, gi = j / per_group, r = j - gi * per_group;
         const int grp = gi * 8 + (blockIdx.x & 7);
         const int b = grp / a.H_kv, hk = grp - b * a.H_kv;
-        run_item(a.n_qtiles - 1 - r / a.group, b * a.H + hk * a.group + r % a.group, 0);   // heaviest first
+        const int t = r / a.group, bh = b * a.H + hk * a.group + r % a.group;
+        const int len = a.cu_q[b + 1] - a.cu_q[b];     // run_item checks the offsets themselves
+        const int nb = (len > 0 && len <= a.max_q) ? (len + BR - 1) / BR : 0;
+        if (t < ((nb + 1) >> 1)) {
+            run_item(nb - 1 - t, bh, 0);
+            if (t != nb - 1 - t) {
+                __syncthreads();    // the next item refills stage0
+                run_item(t, bh, 0);
+            }
+        }
     } else if (CAUSAL && !VARLEN && !SPLIT && a.paired) {
         // Causal query tiles t and n_qtiles-1-t together see a fixed number of key
         // tiles, so pairing them gives every workgroup the same work: the
@@ -462,7 +474,7 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     const int mode = p.varlen ? 2 : (split ? 1 : 0);
     // causal [B,H,N,d]: one workgroup per pair of query tiles (two pairs per
     // workgroup, one dispatch round with no rebalancing, measured slower)
-    a.paired = p.causal && mode == 0 && a.n_qtiles >= 2;
+    a.paired = (p.causal && mode == 0 && a.n_qtiles >= 2) || (mode == 2 && (a.B * a.H_kv) % 8 == 0);
     const int64_t blocks = a.paired ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH : (int64_t)a.n_qtiles * a.BH * S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.d == 128)
