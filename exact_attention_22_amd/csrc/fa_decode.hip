@@ -10,7 +10,8 @@
 // (b, h, split).  A key row of D 16-bit values is spread over D/8 lanes, 16
 // bytes each, so every load instruction of a wavefront reads 1 KiB of
 // consecutive memory (4 rows at d = 128, 8 at d = 64).  The dot product is
-// finished with DPP row operations, every lane of the row keeps the online
+// finished with DPP row operations (the products as fp32 dot products of 16-bit
+// pairs), every lane of the row keeps the online
 // softmax state of its row, and each lane accumulates its own 8 output values.
 // Eight groups of keys are loaded per step so that enough bytes are in flight
 // to cover HBM latency.  At the end the 16 (d = 128) or 32 (d = 64) partial
@@ -82,6 +83,15 @@ __device__ __forceinline__ void widen8(u32x4 x, float* f) {
     }
 }
 
+// a.x * b.x + a.y * b.y + acc over two packed 16-bit values, in fp32.
+template <bool BF16>
+__device__ __forceinline__ float dot2(u32 a, u32 b, float acc) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+
 // GP: query heads per workgroup (a divisor of the group size).  PAGED: k and v
 // are the paged caches.
 template <bool BF16, int D, int GP, bool PAGED>
@@ -127,13 +137,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     // below the sequence length index the block table
     auto page_of = [&](int key) -> int { return key < ke ? bt[key >> a.page_shift] : -1; };
 
-    float qv[GP][8];
+    // this lane's 8 query values per head, kept packed: the score is c times a
+    // dot product of 16-bit pairs accumulated in fp32 (v_dot2_f32_{f16,bf16};
+    // the products are exact in fp32)
+    u32x4 qp[GP];
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
-        widen8<BF16>(*(const u32x4*)(a.q + (size_t)(bh0 + g) * D + 8 * c), qv[g]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[g][i] *= a.c;
-    }
+    for (int g = 0; g < GP; ++g) qp[g] = *(const u32x4*)(a.q + (size_t)(bh0 + g) * D + 8 * c);
 
     float M[GP], l[GP], acc[GP][8];
 #pragma unroll
@@ -184,14 +193,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float kf[8];
-            widen8<BF16>(kr[u], kf);
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
                 float part = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qv[g][i], kf[i], part);
-                s[g][u] = row_sum<CH>(part);
+                for (int i = 0; i < 4; ++i) part = dot2<BF16>(qp[g][i], kr[u][i], part);
+                s[g][u] = row_sum<CH>(part) * a.c;
                 if (!ok[u]) s[g][u] = -INFINITY;
                 mx[g] = fmaxf(mx[g], s[g][u]);
             }
