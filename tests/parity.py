@@ -53,6 +53,32 @@ def sample_rows(B, H, Nq, n_random=256, seed=0):
 GRAD_TOL = {torch.float16: 4 * 2.0 ** -11, torch.bfloat16: 4 * 2.0 ** -8}
 
 
+def d_rounding_shift(q, k, dout, o_ref, lse_ref, causal, scale, dtype):
+    """Exact effect on dQ and dK of forming D = rowsum(dO o O) from O rounded to the
+    output type (the pages' recipe: the backward reads the forward's stored O)
+    instead of the exact O.  With dD_i = sum_t dO_it (round(O_it) - O_it), dS moves
+    by -P_ij dD_i, so dq_i moves by -scale dD_i sum_j P_ij k_j and dk_j by
+    -scale sum_i P_ij dD_i q_i.  dP - D can cancel to far below the gradient's own
+    size, so this term is not covered by a tolerance relative to the gradient;
+    adding it to the oracle's exact gradients compares like with like.  O is the
+    oracle's, rounded here; P is formed in fp64 from the oracle's LSE."""
+    qd, kd, gd = (t.double().cpu().numpy() for t in (q, k, dout))
+    o = np.asarray(o_ref, dtype=np.float64).reshape(qd.shape)
+    o_r = torch.from_numpy(np.ascontiguousarray(o)).to(dtype).double().numpy()
+    lse = np.asarray(lse_ref, dtype=np.float64).reshape(qd.shape[:3])
+    dD = np.sum(gd * (o_r - o), axis=-1)                                       # [B, H, Nq]
+    Nq, Nk = qd.shape[2], kd.shape[2]
+    fin = np.isfinite(lse)
+    vis = np.broadcast_to(fin[..., None], fin.shape + (Nk,)).copy()
+    if causal:
+        vis &= (np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq))[None, None]
+    s = scale * np.einsum("bhid,bhjd->bhij", qd, kd) - np.where(fin, lse, 0.0)[..., None]
+    p = np.where(vis, np.exp(np.where(vis, s, 0.0)), 0.0)
+    ddq = -scale * dD[..., None] * np.einsum("bhij,bhjd->bhid", p, kd)
+    ddk = -scale * np.einsum("bhij,bhi,bhid->bhjd", p, dD, qd)
+    return ddq, ddk
+
+
 def grad_errors(grads, refs):
     out = {}
     for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
