@@ -38,10 +38,17 @@
 //     coalesced buffer loads that write LDS directly and an XOR swizzle
 //     (fa_device.h).
 //   * Lazy rescale: the exponent reference only moves (and O, l are only
-//     rescaled) when a row's new maximum exceeds it by more than 2^8 in
-//     probability, decided per wavefront.  Any reference gives the same
-//     O = sum 2^(t-M) v / sum 2^(t-M); keeping the reference at or below the
-//     true maximum keeps every P <= 256, well inside fp16 range.
+//     rescaled) when it would let a weight grow too large, decided per
+//     wavefront.  Any reference gives the same O = sum 2^(t-M) v / sum 2^(t-M).
+//     Tiles that cross the diagonal or the key tail take the row maximum and
+//     move the reference when it is exceeded by more than 2^8 in probability.
+//     Fully visible tiles skip the maximum: each 32-key block is exponentiated
+//     against the current reference and kept when every lane's sum of its 16
+//     weights stays <= 2^12; otherwise the reference moves to the block's exact
+//     running maximum and the block is exponentiated again (rescaling between
+//     blocks is the online-softmax merge).  The reference is always an observed
+//     maximum, so it never exceeds the true one; every P stays <= 2^12, far
+//     inside fp16 range.
 //   * Workgroups are mapped so that consecutive tiles of one head share an XCD
 //     (and its L2).  Causal [B, H, N, d]: one workgroup runs query tiles
 //     n_qtiles-1-t and t, which together see a fixed number of key tiles, so
@@ -58,6 +65,7 @@ namespace {
 
 constexpr int BR = 128;     // query rows per workgroup (4 waves x 32)
 constexpr int BC = 64;      // keys per tile
+constexpr float SUM_CAP = 4096.f;  // fully visible tiles: largest per-lane sum of 16 weights kept
 constexpr float TAU = 8.0f; // lazy-rescale threshold, log2 units
 
 struct FwdArgs {
@@ -242,6 +250,60 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 }
             }
             after_s();
+            if constexpr (!MASKED) {
+                // Fully visible tile, one 32-key block at a time: exponentiate against
+                // the current reference and keep the block if every lane's partial sum
+                // of its 16 weights stays <= 2^12 (so every weight does) and the
+                // reference is set; otherwise move the reference to the exact running
+                // maximum (rescaling O and l first) and exponentiate the block again.
+                // Rescaling between blocks is the online-softmax merge itself, so no
+                // row maximum is needed while the reference holds.
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    float pv[16];
+                    float t0 = 0.f, t1 = 0.f;
+                    auto expo = [&]() {
+                        const float Mg = (Mu == -INFINITY) ? 0.f : Mu;
+                        t0 = 0.f;
+                        t1 = 0.f;
+    #pragma unroll
+                        for (int r = 0; r < 16; r += 2) {
+                            pv[r] = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
+                            pv[r + 1] = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], a.c, -Mg));
+                            t0 += pv[r];
+                            t1 += pv[r + 1];
+                        }
+                    };
+                    expo();
+                    if (__ballot(!(t0 + t1 <= SUM_CAP) || Mu == -INFINITY)) {
+                        float mx = sacc[kb][0];
+    #pragma unroll
+                        for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sacc[kb][r]);
+                        mx = max_halves(mx);
+                        const float Mn = fmaxf(Mu, (mx == -INFINITY) ? -INFINITY : mx * a.c);
+                        const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
+                        lsum *= alpha;
+    #pragma unroll
+                        for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+                        Mu = Mn;
+                        expo();
+                    }
+                    lsum += t0 + t1;
+    #pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const u32x4 pb = {pack2<BF16>(pv[8 * p + 0], pv[8 * p + 1]), pack2<BF16>(pv[8 * p + 2], pv[8 * p + 3]),
+                                          pack2<BF16>(pv[8 * p + 4], pv[8 * p + 5]), pack2<BF16>(pv[8 * p + 6], pv[8 * p + 7])};
+                        const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
+    #pragma unroll
+                        for (int db = 0; db < ND; ++db) {
+                            const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
+                            const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
+                            oacc[db] = mfma32<BF16>(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb, oacc[db]);
+                        }
+                    }
+                }
+                return;
+            }
             // register r of block kb holds key k0 + 8h + kofs(kb, r); visible iff kofs < bound
             int bound = 0;
             if constexpr (MASKED) {
