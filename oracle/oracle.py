@@ -168,6 +168,33 @@ class Oracle:
                               rows=rows, key_range=key_range, nthreads=nthreads)
 
     # -- packed variable-length sequences, grouped K/V heads -------------
+    def attention_bwd_gqa(self, q, k, v, dout, causal, scale, q_rows=None, k_rows=None, nthreads=None):
+        """attention_bwd() with k, v [B, H_kv, Nk, d] shared by groups of query heads.
+
+        A K/V head enters the loss through each of its G = H // H_kv query heads, so
+        by the chain rule its dK (dV) is the sum of the per-query-head dK (dV) that
+        attention_bwd gives on the expanded heads (KingOfEgg, "Flash Attention (4)",
+        section 5: K/V indexed by head group).  k_rows are flat (b*H_kv + hk)*Nk + j;
+        dq and q_rows are as in attention_bwd.
+        """
+        B, H, Nq, d = q.shape
+        H_kv, Nk = k.shape[1], k.shape[2]
+        if H % H_kv != 0:
+            raise ValueError("H_kv must divide H")
+        G = H // H_kv
+        ke, ve = self.expand_kv_heads(k, H), self.expand_kv_heads(v, H)
+        if k_rows is None:
+            dq, dk, dv = self.attention_bwd(q, ke, ve, dout, causal, scale, q_rows=q_rows, nthreads=nthreads)
+            return dq, dk.reshape(B, H_kv, G, Nk, d).sum(axis=2), dv.reshape(B, H_kv, G, Nk, d).sum(axis=2)
+        kr = np.asarray(k_rows, dtype=np.int64)
+        bh, j = kr // Nk, kr % Nk
+        b, hk = bh // H_kv, bh % H_kv
+        # the G expanded rows of each selected K/V row, group member fastest
+        er = (((b * H + hk * G)[:, None] + np.arange(G)[None, :]) * Nk + j[:, None]).reshape(-1)
+        dq, dk, dv = self.attention_bwd(q, ke, ve, dout, causal, scale, q_rows=q_rows, k_rows=er,
+                                        nthreads=nthreads)
+        return dq, dk.reshape(-1, G, d).sum(axis=1), dv.reshape(-1, G, d).sum(axis=1)
+
     def attention_varlen(self, q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, rows=None,
                          nthreads=None):
         """fp64 attention of packed sequences: q [total_q, H, d] against k, v

@@ -434,6 +434,32 @@ def pin_bwd_autograd(orc):
             _close(dv, rv, 1e-12, f"bwd dV case {ci} {dt}")
 
 
+def pin_bwd_gqa_autograd(orc):
+    """Grouped K/V heads: dK, dV of a shared head equal fp64 autograd through the
+    head expansion (a gather inside the graph, so autograd itself sums the group),
+    full and on selected rows."""
+    for ci, (B, H, H_kv, Nq, Nk, d, causal, scale) in enumerate([
+            (1, 4, 2, 9, 11, 8, True, 0.4), (2, 3, 1, 6, 6, 16, False, -0.7), (1, 4, 1, 5, 12, 8, True, 1.1)]):
+        dt = DTYPES[ci % len(DTYPES)]
+        q, g = (_rand((B, H, Nq, d), dt, 1800 + 10 * ci + s) for s in (0, 1))
+        k, v = (_rand((B, H_kv, Nk, d), dt, 1802 + 10 * ci + s) for s in (0, 1))
+        qd, kd, vd = (t.double().requires_grad_(True) for t in (q, k, v))
+        head = torch.arange(H) // (H // H_kv)
+        vis = torch.from_numpy(_visible(Nq, Nk, causal))
+        sc = float(np.float32(scale)) * (qd @ kd[:, head].transpose(-1, -2))
+        empty = ~vis.any(dim=1)
+        p = torch.softmax(sc.masked_fill(~vis, -math.inf).masked_fill(empty[:, None], 0.0), dim=-1)
+        (p.masked_fill(empty[:, None], 0.0) @ vd[:, head]).backward(g.double())
+        dq, dk, dv = orc.attention_bwd_gqa(q, k, v, g, causal, scale, nthreads=2)
+        _close(dq, qd.grad.numpy(), 1e-12, f"bwd gqa dQ case {ci}")
+        _close(dk, kd.grad.numpy(), 1e-12, f"bwd gqa dK case {ci}")
+        _close(dv, vd.grad.numpy(), 1e-12, f"bwd gqa dV case {ci}")
+        rows = np.array([0, Nk - 1, B * H_kv * Nk - 1, (B * H_kv - 1) * Nk])
+        _, sk, sv = orc.attention_bwd_gqa(q, k, v, g, causal, scale, k_rows=rows, nthreads=2)
+        _close(sk, kd.grad.numpy().reshape(-1, d)[rows], 1e-12, f"bwd gqa dK rows case {ci}")
+        _close(sv, vd.grad.numpy().reshape(-1, d)[rows], 1e-12, f"bwd gqa dV rows case {ci}")
+
+
 def pin_bwd_finite_differences(orc):
     """Central differences of L = sum(O o dO) (O from torch's fp64 attention) match
     the gradients to within the O(h^2) truncation error."""
@@ -702,6 +728,6 @@ ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
             pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows,
-            pin_dense_grouped_heads, pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_scale_zero,
-            pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows, pin_paged_matches_contiguous,
+            pin_dense_grouped_heads, pin_bwd_autograd, pin_bwd_gqa_autograd, pin_bwd_finite_differences,
+            pin_bwd_scale_zero, pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows, pin_paged_matches_contiguous,
             pin_paged_brute_force, pin_paged_empty_sequence, pin_paged_splits]
