@@ -122,19 +122,39 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
     return (size_t)n * 8u;   // D and LSE * log2(e), fp32 each
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                 int B, int H, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+namespace {
+
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int H_kv,
+                   int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
     fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
+    if ((st = check_heads(H, H_kv)) != FA_OK) return st;
     if (workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
         !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 15u) || ((uintptr_t)workspace & 15u))
         return FA_ERR_UNSUPPORTED;
     fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, Nk, d, causal != 0,
-                    dtype == FA_BF16, scale};
+                    dtype == FA_BF16, scale, H_kv};
     return from_hip(fa::launch_bwd(p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, Nq, Nk, d, causal,
+                    scale, dtype, stream);
+}
+
+fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
+                     void* stream) {
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv, Nq, Nk, d, causal,
+                    scale, dtype, stream);
 }
 
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {

@@ -59,6 +59,7 @@ struct BwdArgs {
     uint16_t* dk;
     uint16_t* dv;
     int BH, Nq, Nk;
+    int H, H_kv, group;  // query heads, K/V heads, query heads per K/V head
     float c;             // scale * log2(e), sign included
     float scale;
     int n_qtiles;        // dQ kernel work items per head
@@ -245,8 +246,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
         const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
         const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
-        const uint16_t* kg = a.k + (size_t)bh * Nk * D;
-        const uint16_t* vg = a.v + (size_t)bh * Nk * D;
+        const int bkv = a.group == 1 ? bh : (bh / a.H) * a.H_kv + (bh % a.H) / a.group;   // K/V head read
+        const uint16_t* kg = a.k + (size_t)bkv * Nk * D;
+        const uint16_t* vg = a.v + (size_t)bkv * Nk * D;
 
         int hi = Nk;
         if (CAUSAL) hi = min(hi, min(Nq, q0 + BQ) + off);
@@ -402,10 +404,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
         const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
         const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
-        const uint16_t* qg = a.q + (size_t)bh * Nq * D;
-        const uint16_t* gg = a.dout + (size_t)bh * Nq * D;
-        const float* lg = a.lse2 + (size_t)bh * Nq;
-        const float* dg = a.delta + (size_t)bh * Nq;
+        // bh is the K/V head b*H_kv + hk; its query heads b*H + hk*group + g
+        // (g < group) each add their rows' contributions to dK and dV
+        const size_t bq0 = (size_t)(bh / a.H_kv) * a.H + (size_t)(bh % a.H_kv) * a.group;
 
         // first query row that sees a key of this block, and the query tiles from it
         const int q_lo = CAUSAL ? max(0, k0 - off) : 0;
@@ -425,8 +426,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
         u32 voff[NPW];
         dma_offsets<D, NPW>(w, lane, voff);
-        auto load_tile = [&](int tile, unsigned char* stage) {
+        // the query tile `tile` of query head g of the group
+        auto load_tile = [&](int g, int tile, unsigned char* stage) {
             const int i0 = tile * CQ;
+            const size_t bq = bq0 + g;
+            const uint16_t* qg = a.q + bq * Nq * D;
+            const uint16_t* gg = a.dout + bq * Nq * D;
+            const float* lg = a.lse2 + bq * Nq;
+            const float* dg = a.delta + bq * Nq;
             load_rows<D, NPW>(qg + (size_t)i0 * D, Nq - i0, stage, w, voff);
             load_rows<D, NPW>(gg + (size_t)i0 * D, Nq - i0, stage + QTILE, w, voff);
             // 64 LSE and 64 D values (256 B each) land at lane*16 of a 1 KiB area;
@@ -469,15 +476,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             dkdv_accum<BF16, D>(Qb, Gb, 1, of, pb1, sb1, dkacc, dvacc);
         };
 
-        // query tiles upward from the diagonal: the first ones may hold rows that do
-        // not yet see some keys of the block
-        if (n_tiles > 0) load_tile(t0, stage0);
+        // query tiles upward from the diagonal (the first ones may hold rows that do
+        // not yet see some keys of the block), for each query head of the group in
+        // turn: step it covers head it / n_tiles, tile t0 + it % n_tiles
+        const int n_steps = n_tiles * a.group;
+        if (n_steps > 0) load_tile(0, t0, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         // two tiles per trip, so that each step reads one fixed LDS stage
+        int g_next = 0, t_next = 0;   // head and tile offset of step it + 1
         auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
-            const int tile = t0 + it;
-            if (it + 1 < n_tiles) load_tile(tile + 1, nxt);
+            const int tile = t0 + t_next;
+            if (++t_next == n_tiles) {
+                t_next = 0;
+                ++g_next;
+            }
+            if (it + 1 < n_steps) load_tile(g_next, t0 + t_next, nxt);
             const int i0 = tile * CQ;
             // causal: a wave whose keys every row of the tile sees needs no mask, and
             // one whose keys no row sees yet skips the tile
@@ -487,9 +501,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             __syncthreads();
         };
     #pragma clang loop unroll(disable)
-        for (int it = 0; it < n_tiles; it += 2) {
+        for (int it = 0; it < n_steps; it += 2) {
             one(it, stage0, stage1);
-            if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
+            if (it + 1 < n_steps) one(it + 1, stage1, stage0);
         }
 
         if (kok) {
@@ -509,14 +523,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 }
         }
     };
-    for_items<CAUSAL>(a.n_ktiles, a.BH, run_item);
+    for_items<CAUSAL>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
 }
 
 template <bool BF16, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
     const int64_t dblocks = (rows + 255) / 256;
     hipLaunchKernelGGL((bwd_delta_kernel<BF16, D>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
-    const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH);
+    const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH / a.group);
     const int q_blocks = (int)item_blocks(causal, a.n_qtiles, a.BH);
     if (causal) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true>), dim3(kv_blocks), dim3(256), 0, s, a);
@@ -544,6 +558,9 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.dk = (uint16_t*)p.dk;
     a.dv = (uint16_t*)p.dv;
     a.BH = p.B * p.H;
+    a.H = p.H;
+    a.H_kv = p.H_kv > 0 ? p.H_kv : p.H;
+    a.group = p.H / a.H_kv;
     a.Nq = p.Nq;
     a.Nk = p.Nk;
     a.c = p.scale * kLog2e;

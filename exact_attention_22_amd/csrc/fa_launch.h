@@ -33,8 +33,9 @@ struct FwdParams {
     int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
-// Validated arguments of one backward launch ([B, H, N, d] tensors; delta is
-// the caller's fp32 workspace of B * H * Nq values).
+// Validated arguments of one backward launch (q, o, dout, dq [B, H, Nq, d]; k, v,
+// dk, dv [B, H_kv, Nk, d], H_kv = 0 meaning H; delta is the caller's fp32
+// workspace of 2 * B * H * Nq values).
 struct BwdParams {
     const void* q;
     const void* k;
@@ -50,6 +51,7 @@ struct BwdParams {
     bool causal;
     bool bf16;
     float scale;
+    int H_kv = 0;
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);

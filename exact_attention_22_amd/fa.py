@@ -18,7 +18,7 @@ FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
+           "fa_bwd_gqa", "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -57,6 +57,9 @@ def lib():
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
         L.fa_bwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, f, i, vp]
+        L.fa_bwd_gqa.restype = i
+        L.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, i, f, i,
+                                 vp]
         L.fa_fwd_fp8.restype = i
         L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         L.fa_quantize_fp8.restype = i
@@ -286,8 +289,26 @@ def bwd_workspace_bytes(B, H, Nq):
 
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
         stream=None):
-    """dQ, dK, dV for the upstream gradient dout, from the forward's inputs, o and lse."""
-    (qp, kp, vp), (B, H, Nq, Nk, d) = _qkv(q, k, v)
+    """dQ, dK, dV for the upstream gradient dout, from the forward's inputs, o and lse.
+
+    k and v may carry fewer heads than q (grouped K/V heads, [B, H_kv, Nk, d]): then
+    fa_bwd_gqa runs, and dk and dv have k's shape and sum over each head's group."""
+    grouped = k.dim() == 4 and q.dim() == 4 and k.shape[1] != q.shape[1]
+    return _bwd(grouped, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace, stream)
+
+
+def bwd_gqa(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+            stream=None):
+    """bwd through fa_bwd_gqa whatever the head counts: k, v [B, H_kv, Nk, d]."""
+    return _bwd(True, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace, stream)
+
+
+def _bwd(grouped, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace, stream):
+    if grouped:
+        (qp, kp, vp), (B, H, H_kv, Nq, Nk, d) = _qkv(q, k, v, grouped=True)
+    else:
+        (qp, kp, vp), (B, H, Nq, Nk, d) = _qkv(q, k, v)
+        H_kv = H
     if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
         raise ValueError("o and dout must be [B, H, Nq, d] and lse [B, H, Nq]")
     opp = _dev_tensor(o, "o", q.dtype)
@@ -303,8 +324,13 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
         workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
     wp = _dev_tensor(workspace, "workspace")
     ptrs = [_dev_tensor(t, n, q.dtype) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
-    _check(lib().fa_bwd(qp, kp, vp, opp, gp, lp, *ptrs, wp, workspace.numel() * workspace.element_size(),
-                        B, H, Nq, Nk, d, int(bool(causal)), _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
+    nws = workspace.numel() * workspace.element_size()
+    if grouped:
+        _check(lib().fa_bwd_gqa(qp, kp, vp, opp, gp, lp, *ptrs, wp, nws, B, H, H_kv, Nq, Nk, d,
+                                int(bool(causal)), _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
+    else:
+        _check(lib().fa_bwd(qp, kp, vp, opp, gp, lp, *ptrs, wp, nws, B, H, Nq, Nk, d, int(bool(causal)),
+                            _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
     return dq, dk, dv
 
 

@@ -248,6 +248,22 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  int B, int H, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream);
 
+/*
+ * fa_bwd with K/V heads shared by groups of query heads (GQA; MQA when H_kv = 1):
+ *   q, o, dout, dq  [B, H, Nq, d]      k, v, dk, dv  [B, H_kv, Nk, d]
+ * Query head h reads K/V head h / (H / H_kv), as in fa_fwd_gqa (KingOfEgg, Flash
+ * Attention (4), section 5: K/V index mapped by group).  A shared K/V head feeds
+ * every query head of its group, so its dK and dV are the sums over that group
+ * of the per-head gradients of fa_bwd; the library accumulates them in one pass
+ * over the group's query tiles, in head order, without atomics (deterministic).
+ * Workspace: fa_bwd_workspace_bytes(B, H, Nq).  H % H_kv must be 0, else
+ * FA_ERR_SHAPE.  With H_kv = H this is fa_bwd.
+ */
+fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
+                     void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);
 

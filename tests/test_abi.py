@@ -105,6 +105,23 @@ def test_bwd_validation():
     assert bwd(lse=MIS) == fa.FA_ERR_UNSUPPORTED
 
 
+def bwd_gqa(q=A, k=A, v=A, o=A, g=A, lse=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 20, B=1, H=4, H_kv=2, Nq=64,
+            Nk=64, d=128, causal=1, scale=0.1, dtype=1):
+    return fa.lib().fa_bwd_gqa(q, k, v, o, g, lse, dq, dk, dv, ws, wsb, B, H, H_kv, Nq, Nk, d, causal, scale,
+                               dtype, NULL)
+
+
+def test_bwd_gqa_validation():
+    assert bwd_gqa(dk=NULL) == fa.FA_ERR_NULL
+    assert bwd_gqa(H_kv=3) == fa.FA_ERR_SHAPE
+    assert bwd_gqa(H_kv=0) == fa.FA_ERR_SHAPE
+    assert bwd_gqa(H_kv=8) == fa.FA_ERR_SHAPE
+    assert bwd_gqa(wsb=4 * 64 * 8 - 4) == fa.FA_ERR_WORKSPACE
+    assert bwd_gqa(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_gqa(dtype=7) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_gqa(dv=MIS) == fa.FA_ERR_UNSUPPORTED
+
+
 def varlen(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, B=2, H=4, H_kv=2, total_q=16, total_k=24, max_q=9,
            max_k=13, d=128, causal=1, scale=0.1, dtype=1):
     return fa.lib().fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, H_kv, total_q, total_k, max_q, max_k,

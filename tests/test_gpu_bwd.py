@@ -1,11 +1,11 @@
-"""GPU parity of the backward pass (fa_bwd) through the C ABI against the fp64
-oracle.
+"""GPU parity of the backward pass (fa_bwd, fa_bwd_gqa) through the C ABI against
+the fp64 oracle.
 
 The library's own forward supplies o and lse (the intended use); the oracle
 computes exact gradients from q, k, v and dout alone.  Small shapes (several
 tiles, ragged tails, Nq != Nk, rows that see no key, a single query row) are
-compared on every element; the causal_d128 workload is compared at full size on
-sampled query and key rows.
+compared on every element; the causal_d128 workload and a grouped-head causal
+prefill are compared at full size on sampled query and key rows.
 """
 import math
 
@@ -96,3 +96,65 @@ def test_bwd_workload(dev, oracle_lib):
     qi, ki = torch.from_numpy(qr).to(dev), torch.from_numpy(kr).to(dev)
     parity.check_grads((dq.reshape(-1, w.d)[qi], dk.reshape(-1, w.d)[ki], dv.reshape(-1, w.d)[ki]),
                        (rq, rk, rv), w.dtype, f"bwd {w.name} sampled")
+
+
+GQA_SMALL = [  # B, H, H_kv, Nq, Nk, d, causal, dtype
+    (1, 4, 2, 200, 200, 128, True, BF16),
+    (2, 4, 1, 129, 300, 64, True, F16),      # MQA, Nq < Nk
+    (1, 8, 2, 300, 129, 128, True, F16),     # Nq > Nk: leading rows see no key
+    (1, 6, 3, 64, 65, 64, False, BF16),
+    (1, 4, 4, 150, 150, 128, True, BF16),    # H_kv = H through the grouped entry point
+    (1, 8, 1, 1, 77, 128, False, F16),
+]
+
+
+def run_gqa(dev, q, k, v, g, causal, scale=None):
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    o, lse = fa.fwd_gqa(qd, kd, vd, causal=causal, scale=scale)
+    grads = fa.bwd_gqa(qd, kd, vd, o, lse, gd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return grads
+
+
+@pytest.mark.parametrize("case", GQA_SMALL, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}-{str(c[7])[-4:]}")
+def test_bwd_gqa_small(dev, oracle_lib, case):
+    B, H, H_kv, Nq, Nk, d, causal, dt = case
+    q, g = rnd((B, H, Nq, d), dt, 21), rnd((B, H, Nq, d), dt, 22)
+    k, v = rnd((B, H_kv, Nk, d), dt, 23), rnd((B, H_kv, Nk, d), dt, 24)
+    say(f"fa_bwd_gqa {case}")
+    grads = run_gqa(dev, q, k, v, g, causal)
+    refs = oracle_lib.attention_bwd_gqa(q, k, v, g, causal, 1 / math.sqrt(d))
+    parity.check_grads(grads, refs, dt, f"bwd gqa {case}")
+
+
+def test_bwd_gqa_matches_bwd_when_ungrouped(dev):
+    """With H_kv = H, fa_bwd_gqa and fa_bwd run the same kernels in the same order:
+    the gradients agree bit for bit."""
+    B, H, N, d = 1, 3, 260, 128
+    q, k, v, g = (rnd((B, H, N, d), BF16, s).to(dev) for s in (31, 32, 33, 34))
+    say("fa_bwd_gqa vs fa_bwd, H_kv = H")
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, g, causal=True)
+    b = fa.bwd_gqa(q, k, v, o, lse, g, causal=True)
+    torch.cuda.synchronize()
+    for x, y, n in zip(a, b, ("dq", "dk", "dv")):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), n
+
+
+def test_bwd_gqa_workload(dev, oracle_lib):
+    """Grouped-head causal prefill at full size (B=1, H=32, H_kv=8, N=4096, d=128,
+    bf16), sampled rows of the first and last query and K/V heads."""
+    B, H, H_kv, N, d, dt = 1, 32, 8, 4096, 128, BF16
+    q, g = rnd((B, H, N, d), dt, 41), rnd((B, H, N, d), dt, 42)
+    k, v = rnd((B, H_kv, N, d), dt, 43), rnd((B, H_kv, N, d), dt, 44)
+    scale = 1 / math.sqrt(d)
+    say(f"fa_bwd_gqa B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 causal")
+    dq, dk, dv = run_gqa(dev, q, k, v, g, True)
+    rng = np.random.default_rng(12)
+    qh, kh = np.array([0, B * H - 1]), np.array([0, B * H_kv - 1])
+    qr = np.unique(np.concatenate([qh * N, qh * N + N - 1, qh[rng.integers(0, 2, 48)] * N + rng.integers(0, N, 48)]))
+    kr = np.unique(np.concatenate([kh * N, kh * N + N - 1, kh[rng.integers(0, 2, 48)] * N + rng.integers(0, N, 48)]))
+    rq, rk, rv = oracle_lib.attention_bwd_gqa(q, k, v, g, True, scale, q_rows=qr, k_rows=kr)
+    qi, ki = torch.from_numpy(qr).to(dev), torch.from_numpy(kr).to(dev)
+    parity.check_grads((dq.reshape(-1, d)[qi], dk.reshape(-1, d)[ki], dv.reshape(-1, d)[ki]),
+                       (rq, rk, rv), dt, "bwd gqa H32/8 N4096 sampled")

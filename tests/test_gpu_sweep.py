@@ -149,20 +149,24 @@ def test_sweep_varlen(dev, oracle_lib, case):
 
 
 BWD = [c for c in (draw(5000 + i) for i in range(40)) if c[1] == c[2]][:10]
+BWD_GQA = [c for c in (draw(6000 + i) for i in range(40)) if c[1] != c[2]][:10]
 
 
-@pytest.mark.parametrize("case", BWD, ids=name)
+@pytest.mark.parametrize("case", BWD + BWD_GQA, ids=name)
 def test_sweep_bwd(dev, oracle_lib, case):
-    B, H, _, Nq, Nk, d, causal, dt, scale = case
-    q, k, v = rnd((B, H, Nq, d), dt, 10), rnd((B, H, Nk, d), dt, 11), rnd((B, H, Nk, d), dt, 12)
+    B, H, H_kv, Nq, Nk, d, causal, dt = case[:8]
+    scale = case[8]
+    q, k, v = rnd((B, H, Nq, d), dt, 10), rnd((B, H_kv, Nk, d), dt, 11), rnd((B, H_kv, Nk, d), dt, 12)
     g = rnd((B, H, Nq, d), dt, 13)
-    say(f"fa_fwd + fa_bwd {name(case)}")
+    say(f"fa_fwd_gqa + fa_bwd_gqa {name(case)}")
     qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
-    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
-    grads = fa.bwd(qd, kd, vd, o, lse, gd, causal=causal, scale=scale)
+    o, lse = fa.fwd_gqa(qd, kd, vd, causal=causal, scale=scale)
+    grads = fa.bwd_gqa(qd, kd, vd, o, lse, gd, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    refs = oracle_lib.attention_bwd(q, k, v, g, causal, scale)
-    ro, rl = oracle_lib.attention(q, k, v, causal, scale)
-    ddq, ddk = parity.d_rounding_shift(q, k, g, ro, rl, causal, scale, dt)
+    refs = oracle_lib.attention_bwd_gqa(q, k, v, g, causal, scale)
+    ro, rl = oracle_lib.attention_gqa(q, k, v, causal, scale)
+    ke = oracle_lib.expand_kv_heads(k, H)
+    ddq, ddk = parity.d_rounding_shift(q, ke, g, ro, rl, causal, scale, dt)
+    ddk = ddk.reshape(B, H_kv, H // H_kv, Nk, d).sum(axis=2)
     refs = (refs[0] + ddq.reshape(refs[0].shape), refs[1] + ddk.reshape(refs[1].shape), refs[2])
     parity.check_grads(grads, refs, dt, f"sweep bwd {name(case)}")
