@@ -195,6 +195,32 @@ class Oracle:
                                         nthreads=nthreads)
         return dq, dk.reshape(-1, G, d).sum(axis=1), dv.reshape(-1, G, d).sum(axis=1)
 
+    def attention_bwd_varlen(self, q, k, v, dout, cu_seqlens_q, cu_seqlens_k, causal, scale, nthreads=None):
+        """Gradients for packed variable-length sequences: q, dout [total_q, H, d];
+        k, v [total_k, H_kv, d]; sequence b owns query rows cu_q[b]..cu_q[b+1] and key
+        rows cu_k[b]..cu_k[b+1] and sees nothing else (KingOfEgg, "Flash Attention
+        (4)", section 5: per-sequence offsets; causal bottom-right within a sequence).
+        Sequences never interact, so each is attention_bwd_gqa on its own rows; a
+        query with no key gets dq = 0 and a key no query sees dk = dv = 0.  Returns
+        fp64 dq [total_q, H, d], dk, dv [total_k, H_kv, d]."""
+        total_q, H, d = q.shape
+        total_k, H_kv = k.shape[0], k.shape[1]
+        cq, ck = np.asarray(cu_seqlens_q, dtype=np.int64), np.asarray(cu_seqlens_k, dtype=np.int64)
+        dq = np.zeros((total_q, H, d))
+        dk = np.zeros((total_k, H_kv, d))
+        dv = np.zeros((total_k, H_kv, d))
+        for b in range(len(cq) - 1):
+            q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+            if q1 == q0 or k1 == k0:
+                continue
+            head_major = lambda t, a, z: t[a:z].permute(1, 0, 2).unsqueeze(0).contiguous()
+            gq, gk, gv = self.attention_bwd_gqa(head_major(q, q0, q1), head_major(k, k0, k1), head_major(v, k0, k1),
+                                                head_major(dout, q0, q1), causal, scale, nthreads=nthreads)
+            dq[q0:q1] = gq[0].transpose(1, 0, 2)
+            dk[k0:k1] = gk[0].transpose(1, 0, 2)
+            dv[k0:k1] = gv[0].transpose(1, 0, 2)
+        return dq, dk, dv
+
     def attention_varlen(self, q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, rows=None,
                          nthreads=None):
         """fp64 attention of packed sequences: q [total_q, H, d] against k, v

@@ -460,6 +460,38 @@ def pin_bwd_gqa_autograd(orc):
         _close(sv, vd.grad.numpy().reshape(-1, d)[rows], 1e-12, f"bwd gqa dV rows case {ci}")
 
 
+def pin_bwd_varlen_autograd(orc):
+    """Packed sequences: gradients equal fp64 autograd of one attention over all
+    packed tokens whose mask allows only same-sequence pairs (bottom-right causal
+    within a sequence), grouped K/V heads included; empty sequences on either side."""
+    for ci, (q_lens, k_lens, H, H_kv, d, causal, scale) in enumerate([
+            ([5, 0, 9, 3], [7, 4, 9, 0], 4, 2, 8, True, 0.45),
+            ([6, 11], [6, 11], 2, 1, 16, False, -0.6), ([1, 8, 4], [9, 2, 4], 3, 3, 8, True, 0.9)]):
+        dt = DTYPES[ci % len(DTYPES)]
+        cq, ck = np.concatenate([[0], np.cumsum(q_lens)]), np.concatenate([[0], np.cumsum(k_lens)])
+        tq, tk = int(cq[-1]), int(ck[-1])
+        q, g = (_rand((tq, H, d), dt, 1900 + 10 * ci + s) for s in (0, 1))
+        k, v = (_rand((tk, H_kv, d), dt, 1902 + 10 * ci + s) for s in (0, 1))
+        seq_q, seq_k = np.repeat(np.arange(len(q_lens)), q_lens), np.repeat(np.arange(len(k_lens)), k_lens)
+        pos_q, pos_k = np.arange(tq) - cq[seq_q], np.arange(tk) - ck[seq_k]
+        vis = seq_q[:, None] == seq_k[None, :]
+        if causal:
+            shift = (np.asarray(k_lens) - np.asarray(q_lens))[seq_q]
+            vis &= pos_k[None, :] <= (pos_q + shift)[:, None]
+        vis = torch.from_numpy(vis)
+        qd, kd, vd = (t.double().requires_grad_(True) for t in (q, k, v))
+        head = torch.arange(H) // (H // H_kv)
+        sc = float(np.float32(scale)) * torch.einsum("ihd,jhd->hij", qd, kd[:, head])
+        empty = ~vis.any(dim=1)
+        p = torch.softmax(sc.masked_fill(~vis, -math.inf).masked_fill(empty[:, None], 0.0), dim=-1)
+        o = torch.einsum("hij,jhd->ihd", p.masked_fill(empty[:, None], 0.0), vd[:, head])
+        o.backward(g.double())
+        dq, dk, dv = orc.attention_bwd_varlen(q, k, v, g, cq, ck, causal, scale, nthreads=2)
+        _close(dq, qd.grad.numpy(), 1e-12, f"bwd varlen dQ case {ci}")
+        _close(dk, kd.grad.numpy(), 1e-12, f"bwd varlen dK case {ci}")
+        _close(dv, vd.grad.numpy(), 1e-12, f"bwd varlen dV case {ci}")
+
+
 def pin_bwd_finite_differences(orc):
     """Central differences of L = sum(O o dO) (O from torch's fp64 attention) match
     the gradients to within the O(h^2) truncation error."""
@@ -728,6 +760,6 @@ ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,
             pin_dominant_score, pin_decoders, pin_split_combine, pin_combine_closed_form,
             pin_worked_examples, pin_varlen_per_sequence, pin_varlen_grouped_heads, pin_varlen_rows,
-            pin_dense_grouped_heads, pin_bwd_autograd, pin_bwd_gqa_autograd, pin_bwd_finite_differences,
-            pin_bwd_scale_zero, pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows, pin_paged_matches_contiguous,
-            pin_paged_brute_force, pin_paged_empty_sequence, pin_paged_splits]
+            pin_dense_grouped_heads, pin_bwd_autograd, pin_bwd_gqa_autograd, pin_bwd_varlen_autograd,
+            pin_bwd_finite_differences, pin_bwd_scale_zero, pin_bwd_key_gradient_sums_to_zero, pin_bwd_rows,
+            pin_paged_matches_contiguous, pin_paged_brute_force, pin_paged_empty_sequence, pin_paged_splits]
