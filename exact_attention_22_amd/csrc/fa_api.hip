@@ -157,6 +157,37 @@ fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                     scale, dtype, stream);
 }
 
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, void* workspace, size_t workspace_bytes, int B, int H, int H_kv,
+                        int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                        float scale, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k || !workspace)
+        return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || check_heads(H, H_kv) != FA_OK) return FA_ERR_SHAPE;
+    if (total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1) return FA_ERR_SHAPE;
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_SHAPE;
+    if (count4(total_q, H, d, 1) < 0 || count4(total_k, H_kv, d, 1) < 0) return FA_ERR_SHAPE;
+    if ((int64_t)B * H > INT32_MAX || B == INT32_MAX) return FA_ERR_SHAPE;
+    // a tile (64 rows of H * d values) must lie within a 32-bit byte range
+    if ((int64_t)H * d * 2 * 64 > INT32_MAX) return FA_ERR_SHAPE;
+    if (workspace_bytes < fa_bwd_workspace_bytes(1, H, total_q)) return FA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 15u) || ((uintptr_t)workspace & 15u) ||
+        ((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, max_seqlen_q, max_seqlen_k, d,
+                    causal != 0, dtype == FA_BF16, scale, H_kv};
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    return from_hip(fa::launch_bwd(p, (hipStream_t)stream));
+}
+
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
     if (!supported_d(d) || num_splits < 1) return 0;
     const int64_t n = count4(num_splits, B, H, Nq);

@@ -53,8 +53,8 @@ struct BwdArgs {
     const uint16_t* o;
     const uint16_t* dout;
     const float* lse;
-    float* delta;        // D = rowsum(dO o O), [B, H, Nq]
-    float* lse2;         // LSE * log2(e), [B, H, Nq]
+    float* delta;        // D = rowsum(dO o O), laid out as lse
+    float* lse2;         // LSE * log2(e), laid out as lse
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -64,7 +64,56 @@ struct BwdArgs {
     float scale;
     int n_qtiles;        // dQ kernel work items per head
     int n_ktiles;        // dK/dV kernel work items per head
+    // packed sequences: q, o, dout, dq [total_q, H, d], k, v, dk, dv [total_k,
+    // H_kv, d], lse [H, total_q]; sequence b owns rows cu_q[b]..cu_q[b+1] and
+    // cu_k[b]..cu_k[b+1]; Nq and Nk are then the longest sequence's lengths
+    const int* cu_q;
+    const int* cu_k;
+    int total_q, total_k;
 };
+
+// Rows of one (sequence, query head, K/V head) item: element offsets of its first
+// Q / K row and first LSE entry, row strides in elements, the offset steps to the
+// next query head (Q rows, LSE entries), and the item's lengths.  ok is false
+// for a packed sequence whose offsets fall outside [0, total], decrease or span
+// more than the longest length: its item writes nothing.
+struct Seq {
+    size_t q, k, l, qh, lh;
+    int sq, sk, Nq, Nk;
+    bool ok;
+};
+
+template <int D, bool VARLEN>
+__device__ __forceinline__ Seq seq_of(const BwdArgs& a, int bq, int bkv) {
+    Seq s;
+    if constexpr (VARLEN) {
+        const int b = bq / a.H, h = bq - b * a.H, hk = bkv - b * a.H_kv;
+        const int qs = a.cu_q[b], q1 = a.cu_q[b + 1], ks = a.cu_k[b], k1 = a.cu_k[b + 1];
+        s.ok = 0 <= qs && qs <= q1 && q1 <= a.total_q && q1 - qs <= a.Nq && 0 <= ks && ks <= k1 &&
+               k1 <= a.total_k && k1 - ks <= a.Nk;
+        s.Nq = s.ok ? q1 - qs : 0;
+        s.Nk = s.ok ? k1 - ks : 0;
+        s.q = ((size_t)qs * a.H + h) * D;
+        s.k = ((size_t)ks * a.H_kv + hk) * D;
+        s.l = (size_t)h * a.total_q + qs;
+        s.qh = D;
+        s.lh = a.total_q;
+        s.sq = a.H * D;
+        s.sk = a.H_kv * D;
+    } else {
+        s.ok = true;
+        s.Nq = a.Nq;
+        s.Nk = a.Nk;
+        s.q = (size_t)bq * a.Nq * D;
+        s.k = (size_t)bkv * a.Nk * D;
+        s.l = (size_t)bq * a.Nq;
+        s.qh = (size_t)a.Nq * D;
+        s.lh = a.Nq;
+        s.sq = D;
+        s.sk = D;
+    }
+    return s;
+}
 
 // Row index (within a 32-row block) that accumulator row i stands for: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm_row(int i) {
@@ -72,12 +121,18 @@ __device__ __forceinline__ int perm_row(int i) {
 }
 
 // D_i = sum_t dO[i,t] O[i,t] in fp32, and LSE_i * log2(e), one thread per row.
-template <bool BF16, int D>
+// Packed sequences: thread row = h * total_q + i reads O row (i, h).
+template <bool BF16, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= rows) return;
-    const uint16_t* op = a.o + (size_t)row * D;
-    const uint16_t* gp = a.dout + (size_t)row * D;
+    size_t orow = (size_t)row;
+    if constexpr (VARLEN) {
+        const int64_t h = row / a.total_q;
+        orow = (size_t)(row - h * a.total_q) * a.H + (size_t)h;
+    }
+    const uint16_t* op = a.o + orow * D;
+    const uint16_t* gp = a.dout + orow * D;
     float acc = 0.f;
 #pragma unroll 4
     for (int t = 0; t < D; t += 8) {
@@ -125,26 +180,30 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned char* rows, const Off
 // Fill `nload` 1 KiB chunks of an LDS tile of rows (the wave's share) from
 // global rows through buffer loads that write LDS; rows past the descriptor's
 // record count read as zeros.
+// Rows lie row_bytes apart; the record count ends at the first missing row, so
+// no lane reads past the last present row.
 template <int D, int NPW>
 __device__ __forceinline__ void load_rows(const uint16_t* base, int rows_left, unsigned char* dst_tile, int w,
-                                          const u32 (&voff)[NPW]) {
+                                          const u32 (&voff)[NPW], int row_bytes) {
     // wave-uniform record count (a per-lane value would wrap each load in a
     // readfirstlane loop)
-    const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(rows_left, 0), 64)) * (D * 2);   // tiles hold 64 rows
+    const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(rows_left, 0), 64)) * (u32)row_bytes;   // tiles hold 64 rows
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base, nrec);
     unsigned char* dst = dst_tile + w * NPW * 1024;
 #pragma unroll
     for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
 }
 
+// Global byte offsets (rows row_bytes apart) of the chunks this lane moves into
+// the swizzled LDS tile.
 template <int D, int NPW>
-__device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW]) {
+__device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW], int row_bytes) {
     constexpr int ROWB = D * 2;
 #pragma unroll
     for (int u = 0; u < NPW; ++u) {
         const int pos = (w * NPW + u) * 1024 + lane * 16;
         const int row = pos / ROWB, pchunk = (pos % ROWB) >> 4;
-        voff[u] = (u32)(row * ROWB + ((pchunk ^ swz<D>(row)) << 4));
+        voff[u] = (u32)(row * row_bytes + ((pchunk ^ swz<D>(row)) << 4));
     }
 }
 
@@ -234,7 +293,7 @@ __device__ __forceinline__ void dq_accum(const unsigned char* Kb, int kb, const 
     }
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     constexpr int ROWB = D * 2, TILE = BK * ROWB, NS = D / 16, ND = D / 32;
     constexpr int NPW = TILE / 1024 / 4;
@@ -242,13 +301,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
     auto run_item = [&](const int t, const int bh) __attribute__((always_inline)) {
-        const int qt = a.n_qtiles - 1 - t;               // longest causal rows first
-        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
-        const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-        const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
         const int bkv = a.group == 1 ? bh : (bh / a.H) * a.H_kv + (bh % a.H) / a.group;   // K/V head read
-        const uint16_t* kg = a.k + (size_t)bkv * Nk * D;
-        const uint16_t* vg = a.v + (size_t)bkv * Nk * D;
+        const Seq sg = seq_of<D, VARLEN>(a, bh, bkv);
+        const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
+        const int nqt = VARLEN ? (Nq + BQ - 1) / BQ : a.n_qtiles;
+        if (VARLEN && (!sg.ok || t >= nqt)) return;      // past this sequence's rows
+        const int qt = nqt - 1 - t;                      // longest causal rows first
+        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
+        const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
+        const uint16_t* kg = a.k + sg.k;
+        const uint16_t* vg = a.v + sg.k;
 
         int hi = Nk;
         if (CAUSAL) hi = min(hi, min(Nq, q0 + BQ) + off);
@@ -259,19 +321,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         const bool qok = qi < Nq;
     #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const size_t e = ((size_t)bh * Nq + qi) * D + 16 * s + 8 * h;
+            const size_t e = sg.q + (size_t)qi * sg.sq + 16 * s + 8 * h;
             qf[s] = qok ? *(const u32x4*)(a.q + e) : u32x4{0, 0, 0, 0};
             gf[s] = qok ? *(const u32x4*)(a.dout + e) : u32x4{0, 0, 0, 0};
         }
-        const float lse2 = qok ? a.lse2[(size_t)bh * Nq + qi] : 0.f;
-        const float dlt = qok ? a.delta[(size_t)bh * Nq + qi] : 0.f;
+        const float lse2 = qok ? a.lse2[sg.l + qi] : 0.f;
+        const float dlt = qok ? a.delta[sg.l + qi] : 0.f;
 
         u32 voff[NPW];
-        dma_offsets<D, NPW>(w, lane, voff);
+        dma_offsets<D, NPW>(w, lane, voff, sg.sk * 2);
         auto load_tile = [&](int tile, unsigned char* stage) {
             const int k0 = tile * BK;
-            load_rows<D, NPW>(kg + (size_t)k0 * D, Nk - k0, stage, w, voff);
-            load_rows<D, NPW>(vg + (size_t)k0 * D, Nk - k0, stage + TILE, w, voff);
+            load_rows<D, NPW>(kg + (size_t)k0 * sg.sk, Nk - k0, stage, w, voff, sg.sk * 2);
+            load_rows<D, NPW>(vg + (size_t)k0 * sg.sk, Nk - k0, stage + TILE, w, voff, sg.sk * 2);
         };
         const Offsets<D> of(lane);
 
@@ -331,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
 
         if (qok) {
-            uint16_t* dst = a.dq + ((size_t)bh * Nq + qi) * D;
+            uint16_t* dst = a.dq + sg.q + (size_t)qi * sg.sq;
     #pragma unroll
             for (int db = 0; db < ND; ++db)
     #pragma unroll
@@ -391,7 +453,7 @@ __device__ __forceinline__ void dkdv_accum(const unsigned char* Qb, const unsign
     }
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int ROWB = D * 2, QTILE = CQ * ROWB, NS = D / 16, ND = D / 32;
     constexpr int NPW = QTILE / 1024 / 4;
@@ -401,12 +463,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
     // key tile 0 first: the longest causal columns
     auto run_item = [&](const int kt, const int bh) __attribute__((always_inline)) {
-        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
-        const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
-        const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
         // bh is the K/V head b*H_kv + hk; its query heads b*H + hk*group + g
         // (g < group) each add their rows' contributions to dK and dV
-        const size_t bq0 = (size_t)(bh / a.H_kv) * a.H + (size_t)(bh % a.H_kv) * a.group;
+        const int bq0 = (bh / a.H_kv) * a.H + (bh % a.H_kv) * a.group;
+        const Seq sg = seq_of<D, VARLEN>(a, bq0, bh);
+        const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
+        if (VARLEN && (!sg.ok || kt * CK >= Nk)) return;   // past this sequence's keys
+        const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
+        const int k0 = kt * CK, kw = k0 + 32 * w, kj = kw + l32;
 
         // first query row that sees a key of this block, and the query tiles from it
         const int q_lo = CAUSAL ? max(0, k0 - off) : 0;
@@ -419,23 +483,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const bool kok = kj < Nk;
     #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const size_t e = ((size_t)bh * Nk + kj) * D + 16 * s + 8 * h;
+            const size_t e = sg.k + (size_t)kj * sg.sk + 16 * s + 8 * h;
             kf[s] = kok ? *(const u32x4*)(a.k + e) : u32x4{0, 0, 0, 0};
             vf[s] = kok ? *(const u32x4*)(a.v + e) : u32x4{0, 0, 0, 0};
         }
 
         u32 voff[NPW];
-        dma_offsets<D, NPW>(w, lane, voff);
+        dma_offsets<D, NPW>(w, lane, voff, sg.sq * 2);
         // the query tile `tile` of query head g of the group
         auto load_tile = [&](int g, int tile, unsigned char* stage) {
             const int i0 = tile * CQ;
-            const size_t bq = bq0 + g;
-            const uint16_t* qg = a.q + bq * Nq * D;
-            const uint16_t* gg = a.dout + bq * Nq * D;
-            const float* lg = a.lse2 + bq * Nq;
-            const float* dg = a.delta + bq * Nq;
-            load_rows<D, NPW>(qg + (size_t)i0 * D, Nq - i0, stage, w, voff);
-            load_rows<D, NPW>(gg + (size_t)i0 * D, Nq - i0, stage + QTILE, w, voff);
+            const uint16_t* qg = a.q + sg.q + g * sg.qh;
+            const uint16_t* gg = a.dout + sg.q + g * sg.qh;
+            const float* lg = a.lse2 + sg.l + g * sg.lh;
+            const float* dg = a.delta + sg.l + g * sg.lh;
+            load_rows<D, NPW>(qg + (size_t)i0 * sg.sq, Nq - i0, stage, w, voff, sg.sq * 2);
+            load_rows<D, NPW>(gg + (size_t)i0 * sg.sq, Nq - i0, stage + QTILE, w, voff, sg.sq * 2);
             // 64 LSE and 64 D values (256 B each) land at lane*16 of a 1 KiB area;
             // lanes past 64 rows read zeros
             const u32 nrec = (u32)__builtin_amdgcn_readfirstlane(min(max(Nq - i0, 0), CQ)) * 4;
@@ -507,8 +570,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
 
         if (kok) {
-            uint16_t* dkp = a.dk + ((size_t)bh * Nk + kj) * D;
-            uint16_t* dvp = a.dv + ((size_t)bh * Nk + kj) * D;
+            uint16_t* dkp = a.dk + sg.k + (size_t)kj * sg.sk;
+            uint16_t* dvp = a.dv + sg.k + (size_t)kj * sg.sk;
     #pragma unroll
             for (int db = 0; db < ND; ++db)
     #pragma unroll
@@ -526,20 +589,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for_items<CAUSAL>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
     const int64_t dblocks = (rows + 255) / 256;
-    hipLaunchKernelGGL((bwd_delta_kernel<BF16, D>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL((bwd_delta_kernel<BF16, D, VARLEN>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
     const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH / a.group);
     const int q_blocks = (int)item_blocks(causal, a.n_qtiles, a.BH);
     if (causal) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true>), dim3(kv_blocks), dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true>), dim3(q_blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true, VARLEN>), dim3(kv_blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, VARLEN>), dim3(q_blocks), dim3(256), 0, s, a);
     } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, false>), dim3(kv_blocks), dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false>), dim3(q_blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, false, VARLEN>), dim3(kv_blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, VARLEN>), dim3(q_blocks), dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t launch_bwd_v(const BwdArgs& a, int d, bool bf16, bool causal, int64_t rows, hipStream_t stream) {
+    if (d == 128) return bf16 ? launch_bwd_t<true, 128, VARLEN>(a, causal, rows, stream)
+                              : launch_bwd_t<false, 128, VARLEN>(a, causal, rows, stream);
+    return bf16 ? launch_bwd_t<true, 64, VARLEN>(a, causal, rows, stream)
+                : launch_bwd_t<false, 64, VARLEN>(a, causal, rows, stream);
 }
 
 }  // namespace
@@ -553,7 +624,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.dout = (const uint16_t*)p.dout;
     a.lse = p.lse;
     a.delta = p.delta;
-    a.lse2 = p.delta + (size_t)p.B * p.H * p.Nq;
+    const bool varlen = p.cu_q != nullptr;
+    // LSE, D and LSE * log2(e) rows: [B, H, Nq], or [H, total_q] for packed sequences
+    const int64_t rows = varlen ? (int64_t)p.H * p.total_q : (int64_t)p.B * p.H * p.Nq;
+    a.lse2 = p.delta + rows;
+    a.cu_q = p.cu_q;
+    a.cu_k = p.cu_k;
+    a.total_q = p.total_q;
+    a.total_k = p.total_k;
     a.dq = (uint16_t*)p.dq;
     a.dk = (uint16_t*)p.dk;
     a.dv = (uint16_t*)p.dv;
@@ -567,14 +645,11 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.scale = p.scale;
     a.n_qtiles = (p.Nq + BQ - 1) / BQ;
     a.n_ktiles = (p.Nk + CK - 1) / CK;
-    const int64_t rows = (int64_t)a.BH * p.Nq;
     if ((int64_t)a.n_qtiles * a.BH > 0x7fffffff || (int64_t)a.n_ktiles * a.BH > 0x7fffffff ||
         (rows + 255) / 256 > 0x7fffffff)
         return hipErrorInvalidValue;
-    if (p.d == 128) return p.bf16 ? launch_bwd_t<true, 128>(a, p.causal, rows, stream)
-                                  : launch_bwd_t<false, 128>(a, p.causal, rows, stream);
-    return p.bf16 ? launch_bwd_t<true, 64>(a, p.causal, rows, stream)
-                  : launch_bwd_t<false, 64>(a, p.causal, rows, stream);
+    return varlen ? launch_bwd_v<true>(a, p.d, p.bf16, p.causal, rows, stream)
+                  : launch_bwd_v<false>(a, p.d, p.bf16, p.causal, rows, stream);
 }
 
 }  // namespace fa

@@ -52,6 +52,12 @@ struct BwdParams {
     bool bf16;
     float scale;
     int H_kv = 0;
+    // packed sequences (non-null cu_q): q, o, dout, dq [total_q, H, d], k, v, dk,
+    // dv [total_k, H_kv, d], lse [H, total_q]; B sequences with offsets cu_q,
+    // cu_k [B + 1] on the device; Nq, Nk the longest sequence's lengths
+    const int* cu_q = nullptr;
+    const int* cu_k = nullptr;
+    int total_q = 0, total_k = 0;
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);

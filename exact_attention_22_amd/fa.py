@@ -18,7 +18,7 @@ FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_bwd_gqa", "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
+           "fa_bwd_gqa", "fa_bwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -60,6 +60,9 @@ def lib():
         L.fa_bwd_gqa.restype = i
         L.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, i, f, i,
                                  vp]
+        L.fa_bwd_varlen.restype = i
+        L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                    i, i, i, i, i, i, i, i, i, f, i, vp]
         L.fa_fwd_fp8.restype = i
         L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         L.fa_quantize_fp8.restype = i
@@ -331,6 +334,45 @@ def _bwd(grouped, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace, s
     else:
         _check(lib().fa_bwd(qp, kp, vp, opp, gp, lp, *ptrs, wp, nws, B, H, Nq, Nk, d, int(bool(causal)),
                             _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
+               scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of fwd_varlen: q, o, dout [total_q, H, d], k, v [total_k, H_kv, d],
+    lse [H, total_q] as fwd_varlen returned it.  Returns dq, dk, dv shaped like q,
+    k, v (dk, dv summed over each K/V head's group)."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [total_q, H, d] and k, v [total_k, H_kv, d]")
+    total_q, H, d = q.shape
+    total_k, H_kv = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (total_k, H_kv, d) or tuple(v.shape) != (total_k, H_kv, d):
+        raise ValueError("k and v must be [total_k, H_kv, d] with q's d")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (H, total_q):
+        raise ValueError("o and dout must be [total_q, H, d] and lse [H, total_q]")
+    if cu_seqlens_q.dim() != 1 or tuple(cu_seqlens_k.shape) != tuple(cu_seqlens_q.shape):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    B = cu_seqlens_q.shape[0] - 1
+    qp, kp, vp, opp, gp = (_dev_tensor(t, n, q.dtype) for t, n in
+                           ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")))
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    cqp = _dev_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    ckp = _dev_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(v.shape):
+        raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(1, H, total_q) // 4, dtype=torch.float32, device=q.device)
+    wp = _dev_tensor(workspace, "workspace")
+    ptrs = [_dev_tensor(t, n, q.dtype) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _check(lib().fa_bwd_varlen(qp, kp, vp, opp, gp, lp, *ptrs, cqp, ckp, wp,
+                               workspace.numel() * workspace.element_size(), B, H, H_kv, total_q, total_k,
+                               int(max_seqlen_q), int(max_seqlen_k), d, int(bool(causal)), _scale(scale, d),
+                               _DTYPES[q.dtype], _stream(stream)))
     return dq, dk, dv
 
 

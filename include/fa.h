@@ -264,6 +264,27 @@ fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                      int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
                      void* stream);
 
+/*
+ * fa_bwd for packed variable-length sequences with grouped K/V heads: the
+ * gradients of fa_fwd_varlen (same layouts, offsets and causal alignment; see
+ * there), each sequence on its own rows (KingOfEgg, Flash Attention (4), section
+ * 5: per-sequence offsets; Ringi, Lecture 25, section 3.3 for the gradients):
+ *   q, o, dout, dq  [total_q, H, d]     dtype
+ *   k, v, dk, dv    [total_k, H_kv, d]  dtype (dk, dv summed over each group)
+ *   lse             [H, total_q]        float32, as fa_fwd_varlen wrote it
+ * A query that sees no key gets dq = 0; a key that no query sees gets dk = dv = 0.
+ * Workspace: fa_bwd_workspace_bytes(1, H, total_q) bytes, 16-byte aligned.
+ * Requirements as fa_fwd_varlen, and H * d * 128 < 2^31.  The offsets are not
+ * read by the host: a sequence whose offsets fall outside [0, total], decrease,
+ * or span more than max_seqlen leaves its rows of dq, dk, dv unwritten and no
+ * memory outside the tensors is accessed.  Deterministic (no atomics).
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, void* workspace, size_t workspace_bytes, int B, int H, int H_kv,
+                        int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                        float scale, fa_dtype dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);
 

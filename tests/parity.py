@@ -80,11 +80,21 @@ def d_rounding_shift(q, k, dout, o_ref, lse_ref, causal, scale, dtype):
 
 
 def grad_errors(grads, refs):
+    """Max error of each gradient normalised by its reference's largest value.
+
+    dQ and dK vanish exactly when every softmax row is one-hot (a query that sees
+    a single key): dP - D is then zero in exact arithmetic, and the kernel returns
+    the fp32 rounding of that difference.  So their normaliser never drops below
+    2^-10 of dV's largest value (dV = P^T dO keeps the size of dO): that noise is
+    about d * 2^-24 * |dO| |V|, far below the bound this leaves."""
     out = {}
+    dv_max = float(np.max(np.abs(refs[2]), initial=0.0))
     for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
         a = g.detach().double().cpu().numpy().reshape(r.shape)
         assert not np.isnan(a).any(), f"NaN in {name}"
         scale = max(float(np.max(np.abs(r), initial=0.0)), 1e-30)
+        if name != "dv":
+            scale = max(scale, 2.0 ** -10 * dv_max)
         out[name] = float(np.max(np.abs(a - r), initial=0.0)) / scale
     return out
 
@@ -95,3 +105,22 @@ def check_grads(grads, refs, dtype, what=""):
     for name, err in e.items():
         assert err <= GRAD_TOL[dtype], f"{what}: {name} normalised error {err:.3e}"
     return e
+
+
+def varlen_bwd_refs(orc, q, k, v, g, cq, ck, causal, scale, dt):
+    """Oracle gradients plus, per sequence, the exact effect of D from rounded O."""
+    rq, rk, rv = orc.attention_bwd_varlen(q, k, v, g, cq.numpy(), ck.numpy(), causal, scale)
+    ro, rl = orc.attention_varlen(q, k, v, cq.numpy(), ck.numpy(), causal, scale)
+    H, H_kv, d = q.shape[1], k.shape[1], q.shape[2]
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        if q1 == q0 or k1 == k0:
+            continue
+        hm = lambda t, a, z: t[a:z].permute(1, 0, 2).unsqueeze(0).contiguous()
+        ke = orc.expand_kv_heads(hm(k, k0, k1), H)
+        ddq, ddk = d_rounding_shift(hm(q, q0, q1), ke, hm(g, q0, q1),
+                                    np.asarray(ro)[q0:q1].transpose(1, 0, 2)[None],
+                                    np.asarray(rl)[:, q0:q1][None], causal, scale, dt)
+        rq[q0:q1] += ddq[0].transpose(1, 0, 2)
+        rk[k0:k1] += ddk[0].reshape(H_kv, H // H_kv, k1 - k0, d).sum(axis=1).transpose(1, 0, 2)
+    return rq, rk, rv

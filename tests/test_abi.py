@@ -122,6 +122,25 @@ def test_bwd_gqa_validation():
     assert bwd_gqa(dv=MIS) == fa.FA_ERR_UNSUPPORTED
 
 
+def bwd_varlen(q=A, k=A, v=A, o=A, g=A, lse=A, dq=A, dk=A, dv=A, cq=A, ck=A, ws=A, wsb=1 << 20, B=2, H=4,
+               H_kv=2, total_q=16, total_k=24, max_q=9, max_k=13, d=128, causal=1, scale=0.1, dtype=1):
+    return fa.lib().fa_bwd_varlen(q, k, v, o, g, lse, dq, dk, dv, cq, ck, ws, wsb, B, H, H_kv, total_q, total_k,
+                                  max_q, max_k, d, causal, scale, dtype, NULL)
+
+
+def test_bwd_varlen_validation():
+    assert bwd_varlen(ck=NULL) == fa.FA_ERR_NULL
+    assert bwd_varlen(ws=NULL) == fa.FA_ERR_NULL
+    assert bwd_varlen(H_kv=3) == fa.FA_ERR_SHAPE
+    assert bwd_varlen(max_q=17) == fa.FA_ERR_SHAPE
+    assert bwd_varlen(total_k=0) == fa.FA_ERR_SHAPE
+    assert bwd_varlen(B=0) == fa.FA_ERR_SHAPE
+    assert bwd_varlen(wsb=4 * 16 * 8 - 4) == fa.FA_ERR_WORKSPACE
+    assert bwd_varlen(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_varlen(cq=ctypes.c_void_p(0x10002)) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_varlen(dk=MIS) == fa.FA_ERR_UNSUPPORTED
+
+
 def varlen(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, B=2, H=4, H_kv=2, total_q=16, total_k=24, max_q=9,
            max_k=13, d=128, causal=1, scale=0.1, dtype=1):
     return fa.lib().fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, H_kv, total_q, total_k, max_q, max_k,

@@ -57,7 +57,7 @@ SMALL = [  # B, H, Nq, Nk, d, causal, dtype
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:5])) + f"-c{int(c[5])}-{str(c[6])[-4:]}")
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:5])) + f"-c{int(c[5])}-{('bf16' if c[6] == BF16 else 'f16')}")
 def test_bwd_small(dev, oracle_lib, case):
     B, H, Nq, Nk, d, causal, dt = case
     q, k, v = rnd((B, H, Nq, d), dt, 1), rnd((B, H, Nk, d), dt, 2), rnd((B, H, Nk, d), dt, 3)
@@ -116,7 +116,7 @@ def run_gqa(dev, q, k, v, g, causal, scale=None):
     return grads
 
 
-@pytest.mark.parametrize("case", GQA_SMALL, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}-{str(c[7])[-4:]}")
+@pytest.mark.parametrize("case", GQA_SMALL, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}-{('bf16' if c[7] == BF16 else 'f16')}")
 def test_bwd_gqa_small(dev, oracle_lib, case):
     B, H, H_kv, Nq, Nk, d, causal, dt = case
     q, g = rnd((B, H, Nq, d), dt, 21), rnd((B, H, Nq, d), dt, 22)

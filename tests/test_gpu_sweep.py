@@ -170,3 +170,21 @@ def test_sweep_bwd(dev, oracle_lib, case):
     ddk = ddk.reshape(B, H_kv, H // H_kv, Nk, d).sum(axis=2)
     refs = (refs[0] + ddq.reshape(refs[0].shape), refs[1] + ddk.reshape(refs[1].shape), refs[2])
     parity.check_grads(grads, refs, dt, f"sweep bwd {name(case)}")
+
+
+@pytest.mark.parametrize("case", VARLEN[:10], ids=lambda c: f"q{c[0]}k{c[1]}H{c[2]}kv{c[3]}d{c[4]}c{int(c[5])}")
+def test_sweep_bwd_varlen(dev, oracle_lib, case):
+    q_lens, k_lens, H, H_kv, d, causal, dt = case
+    cq, ck = cu_seqlens(q_lens), cu_seqlens(k_lens)
+    tq, tk = int(cq[-1]), int(ck[-1])
+    q, g = rnd((tq, H, d), dt, 14), rnd((tq, H, d), dt, 15)
+    k, v = rnd((tk, H_kv, d), dt, 16), rnd((tk, H_kv, d), dt, 17)
+    scale = 1 / math.sqrt(d)
+    say(f"fa_fwd_varlen + fa_bwd_varlen q={q_lens} k={k_lens} H={H} H_kv={H_kv} d={d} causal={causal} {dt}")
+    max_q, max_k = max(q_lens), max(max(k_lens), 1)
+    qd, kd, vd, gd, cqd, ckd = (t.to(dev) for t in (q, k, v, g, cq, ck))
+    o, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, max_q, max_k, causal=causal)
+    grads = fa.bwd_varlen(qd, kd, vd, o, lse, gd, cqd, ckd, max_q, max_k, causal=causal)
+    torch.cuda.synchronize()
+    refs = parity.varlen_bwd_refs(oracle_lib, q, k, v, g, cq, ck, causal, scale, dt)
+    parity.check_grads(grads, refs, dt, f"sweep bwd varlen q={q_lens} k={k_lens}")

@@ -64,7 +64,7 @@ SMALL = [  # q lens, k lens, H, H_kv, d, causal, dtype
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"H{c[2]}kv{c[3]}d{c[4]}c{int(c[5])}-{str(c[6])[-4:]}-{len(c[0])}seq")
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"H{c[2]}kv{c[3]}d{c[4]}c{int(c[5])}-{('bf16' if c[6] == BF16 else 'f16')}-{len(c[0])}seq")
 def test_varlen_small(dev, oracle_lib, case):
     q_lens, k_lens, H, H_kv, d, causal, dt = case
     q, k, v, cq, ck = packed(q_lens, k_lens, H, H_kv, d, dt, 11)
