@@ -211,12 +211,15 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW], i
 // an XCD's L2), `per_head` tiles per head, tile index in the order given (the
 // longest causal tile first).  PAIR (causal): the workgroup runs tiles t and
 // per_head-1-t, which together carry a fixed amount of work, so the XCD
-// round-robin dispatcher never stalls on one XCD's long tile.
-template <bool PAIR, class F>
+// round-robin dispatcher never stalls on one XCD's long tile.  XCD = false keeps
+// the dispatcher's own round-robin order instead: packed sequences differ in
+// work by orders of magnitude, and contiguous ranges would put a long sequence's
+// heads on one XCD.
+template <bool PAIR, bool XCD = true, class F>
 __device__ __forceinline__ void for_items(int per_head, int BH, F&& item) {
     const int total = gridDim.x;
     int L = blockIdx.x;
-    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    if (XCD && (total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
     if (PAIR && per_head >= 2) {
         const int npairs = (per_head + 1) >> 1;
         const int t = L % npairs, bh = L / npairs;
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                 }
         }
     };
-    for_items<CAUSAL>(a.n_qtiles, a.BH, run_item);
+    for_items<CAUSAL, !VARLEN>(a.n_qtiles, a.BH, run_item);
 }
 
 // ---- dK, dV -------------------------------------------------------------------
@@ -586,7 +589,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 }
         }
     };
-    for_items<CAUSAL>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
+    for_items<CAUSAL, !VARLEN>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
 }
 
 template <bool BF16, int D, bool VARLEN>
