@@ -173,8 +173,10 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, 
     qp, kp, vp = (_dev_tensor(t, n, q.dtype) for t, n in ((q, "q"), (k, "k"), (v, "v")))
     cqp = _dev_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     ckp = _dev_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    # rows of a sequence whose offsets break the contract are left unwritten by the
+    # library; outputs allocated here start as O = 0, LSE = -inf (no visible key)
+    out = torch.zeros_like(q) if out is None else out
+    lse = torch.full((H, total_q), -math.inf, dtype=torch.float32, device=q.device) if lse is None else lse
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (H, total_q):
         raise ValueError("out must be [total_q, H, d] and lse [H, total_q]")
     op = _dev_tensor(out, "out", q.dtype)
@@ -246,10 +248,12 @@ def fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits, s
     btp = _dev_tensor(block_table, "block_table", torch.int32)
     slp = _dev_tensor(seqlens_k, "seqlens_k", torch.int32)
     S = int(num_splits)
+    # a sequence whose length breaks the contract leaves its partials unwritten;
+    # partials allocated here start as empty splits (O = 0, LSE = -inf)
     if o_part is None:
-        o_part = torch.empty((S, B, H, 1, d), dtype=torch.float32, device=q.device)
+        o_part = torch.zeros((S, B, H, 1, d), dtype=torch.float32, device=q.device)
     if lse_part is None:
-        lse_part = torch.empty((S, B, H, 1), dtype=torch.float32, device=q.device)
+        lse_part = torch.full((S, B, H, 1), -math.inf, dtype=torch.float32, device=q.device)
     if tuple(o_part.shape) != (S, B, H, 1, d) or tuple(lse_part.shape) != (S, B, H, 1):
         raise ValueError("o_part must be [S, B, H, 1, d] and lse_part [S, B, H, 1]")
     opp = _dev_tensor(o_part, "o_part", torch.float32)
@@ -360,9 +364,11 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
     lp = _dev_tensor(lse, "lse", torch.float32)
     cqp = _dev_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     ckp = _dev_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    # rows of a sequence whose offsets break the contract are left unwritten by the
+    # library; gradients allocated here start at zero
+    dq = torch.zeros_like(q) if dq is None else dq
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(v) if dv is None else dv
     if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(v.shape):
         raise ValueError("dq, dk, dv must have the shapes of q, k, v")
     if workspace is None:

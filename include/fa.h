@@ -104,8 +104,10 @@ fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float
  * H % H_kv == 0, 1 <= max_seqlen_q <= total_q, 1 <= max_seqlen_k <= total_k;
  * cu_seqlens 4-byte aligned.  The offsets live on the device and are not read by
  * the host: a sequence whose offsets fall outside [0, total], decrease, or span
- * more than max_seqlen is skipped by the kernel (its rows of o and lse are left
- * unwritten) and no memory outside the tensors is accessed.
+ * more than max_seqlen is skipped by the kernel: its rows of o and lse keep
+ * whatever the caller's buffers held before the call (the library neither clears
+ * nor reports them; a caller that cannot vouch for its offsets clears o to 0 and
+ * lse to -inf first), and no memory outside the tensors is accessed.
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k,
@@ -167,8 +169,10 @@ fa_status fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v,
  * num_splits >= 1, max_pages * page_size <= INT32_MAX; block_table and
  * seqlens_k 4-byte aligned.  The table and lengths live on the device and are
  * not read by the host: a length outside [0, max_pages * page_size] leaves that
- * sequence's partials unwritten, and a page entry outside [0, num_pages) drops
- * its keys; no memory outside the tensors is accessed.
+ * sequence's partials as the caller's buffers held them (clear o_part to 0 and
+ * lse_part to -inf first to have such a sequence combine to O = 0, LSE = -inf),
+ * and a page entry outside [0, num_pages) drops its keys; no memory outside the
+ * tensors is accessed.
  */
 fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
                                const int* block_table, const int* seqlens_k,
@@ -276,8 +280,9 @@ fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
  * Workspace: fa_bwd_workspace_bytes(1, H, total_q) bytes, 16-byte aligned.
  * Requirements as fa_fwd_varlen, and H * d * 128 < 2^31.  The offsets are not
  * read by the host: a sequence whose offsets fall outside [0, total], decrease,
- * or span more than max_seqlen leaves its rows of dq, dk, dv unwritten and no
- * memory outside the tensors is accessed.  Deterministic (no atomics).
+ * or span more than max_seqlen leaves its rows of dq, dk, dv as the caller's
+ * buffers held them (not cleared, not reported) and no memory outside the
+ * tensors is accessed.  Deterministic (no atomics).
  */
 fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens_q,

@@ -105,7 +105,7 @@ def dequantize(codes, descale, block_rows):
     return vals * np.asarray(descale, dtype=np.float64)[:, rows][:, :, None]
 
 
-def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, rows=None):
+def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, rows=None, spread=False):
     """fp64 attention of dequantized e4m3 inputs.
 
     q8 [B, H, Nq, d], k8 and v8 [B, H_kv, Nk, d] (uint8 codes); q_descale
@@ -120,6 +120,14 @@ def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, ro
     magnitude) and U[r, t] = sum over keys with p_j / max p < 2^-10 of |v_jt|,
     divided by l (the magnitude carried by weights small enough to reach e4m3's
     subnormal range); p_j = exp(s_j - m).
+
+    With spread=True a fifth array shaped like o is returned:
+    R[r, t] = sqrt(sum_j (e_j v_jt)^2) / l with e_j = max(2^-4 p_j, 2^-14), the
+    largest absolute error of p_j rounded to e4m3 (relative 2^-4 for normals;
+    below 2^-10 of the row maximum the absolute spacing takes over, 2^-14 in
+    units of the largest weight).  If each weight's rounding error is spread
+    evenly over that interval, independently of the others, the output error
+    O_t - O_exact,t has a standard deviation of at most R / sqrt(3).
     """
     q8, k8, v8 = (np.asarray(t, dtype=np.uint8) for t in (q8, k8, v8))
     B, H, Nq, d = q8.shape
@@ -134,6 +142,7 @@ def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, ro
     lse = np.full(flat.size, -np.inf)
     amag = np.zeros((flat.size, d))
     umag = np.zeros((flat.size, d))
+    rms = np.zeros((flat.size, d))
     cache = {}
     for r, f in enumerate(flat):
         bh, i = divmod(int(f), Nq)
@@ -156,7 +165,12 @@ def attention_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale, ro
         lse[r] = m + math.log(l)
         amag[r] = (p @ np.abs(vx[:hi])) / l
         umag[r] = np.abs(vx[:hi])[p < 2.0 ** -10].sum(axis=0) / l
+        if spread:
+            e = np.maximum(2.0 ** -4 * p, 2.0 ** -14)
+            rms[r] = np.sqrt((e * e) @ (vx[:hi] * vx[:hi])) / l
     if rows is None:
         sh = (B, H, Nq, d)
-        return o.reshape(sh), lse.reshape(B, H, Nq), amag.reshape(sh), umag.reshape(sh)
-    return o, lse, amag, umag
+        out = (o.reshape(sh), lse.reshape(B, H, Nq), amag.reshape(sh), umag.reshape(sh), rms.reshape(sh))
+    else:
+        out = (o, lse, amag, umag, rms)
+    return out if spread else out[:4]

@@ -754,7 +754,49 @@ def pin_fp8_attention_matches_fp16(orc):
         assert np.all(amag + 1e-12 >= np.abs(o)), "sum p|v|/l bounds |O|"
 
 
-FP8_PINS = [pin_e4m3_decode, pin_e4m3_encode, pin_fp8_quantize_blocks, pin_fp8_attention_matches_fp16]
+def pin_fp8_error_terms(orc=None):
+    """A, U and R of one row worked by hand.  Query (1, 0, ...), keys with first
+    coordinates 0, -11 and -9 (all exact e4m3 codes, scales 1), scale sigma =
+    float32(ln 2): the scores are 0, -11 sigma, -9 sigma, so the weights relative
+    to the maximum are p = (1, e^-11sigma, e^-9sigma) ~ (1, 2^-11, 2^-9); only the
+    second lies below 2^-10.  Values v_j = (1, 2, -4) in the first column and
+    (0, 0, 0.5) in the second:
+        l = 1 + p1 + p2;  O = ((1 + 2 p1 - 4 p2) / l, 0.5 p2 / l)
+        A = ((1 + 2 p1 + 4 p2) / l, 0.5 p2 / l);  U = (2 / l, 0)
+        R = (sqrt(2^-8 + (2^-14 * 2)^2 + (2^-4 p2 * 4)^2) / l, 2^-4 p2 * 0.5 / l)
+    (R's rounding bound is e_j = max(2^-4 p_j, 2^-14): 2^-4 for the largest
+    weight, 2^-14 for p1 < 2^-10, 2^-4 p2 for p2)."""
+    from oracle import fp8
+    d = 16
+    code = lambda x: int(fp8.encode_e4m3(np.array([x]))[0])      # noqa: E731
+    q8 = np.zeros((1, 1, 1, d), dtype=np.uint8)
+    q8[0, 0, 0, 0] = code(1.0)
+    k8 = np.zeros((1, 1, 3, d), dtype=np.uint8)
+    v8 = np.zeros((1, 1, 3, d), dtype=np.uint8)
+    for j, (kk, v0, v1) in enumerate(((0.0, 1.0, 0.0), (-11.0, 2.0, 0.0), (-9.0, -4.0, 0.5))):
+        k8[0, 0, j, 0], v8[0, 0, j, 0], v8[0, 0, j, 1] = code(kk), code(v0), code(v1)
+    one = lambda *shape: np.ones(shape, dtype=np.float32)       # noqa: E731
+    sig = float(np.float32(math.log(2.0)))
+    o, lse, A, U, R = fp8.attention_fp8(q8, k8, v8, one(1, 1, 1), one(1, 1, 1), one(1, 1), False,
+                                        math.log(2.0), spread=True)
+    p1, p2 = math.exp(-11 * sig), math.exp(-9 * sig)
+    assert p1 < 2.0 ** -10 <= p2
+    l = 1 + p1 + p2
+    want = {
+        "O": (o, [(1 + 2 * p1 - 4 * p2) / l, 0.5 * p2 / l]),
+        "A": (A, [(1 + 2 * p1 + 4 * p2) / l, 0.5 * p2 / l]),
+        "U": (U, [2 / l, 0.0]),
+        "R": (R, [math.sqrt(2.0 ** -8 + (2.0 ** -14 * 2) ** 2 + (2.0 ** -4 * p2 * 4) ** 2) / l,
+                  2.0 ** -4 * p2 * 0.5 / l]),
+    }
+    for name, (got, exp) in want.items():
+        _close(got[0, 0, 0, :2], exp, 1e-15, f"fp8 {name}")
+        assert not np.any(got[0, 0, 0, 2:]), f"fp8 {name}: columns with zero values"
+    _close(lse[0, 0, 0], math.log(l), 1e-15, "fp8 LSE")
+
+
+FP8_PINS = [pin_e4m3_decode, pin_e4m3_encode, pin_fp8_quantize_blocks, pin_fp8_attention_matches_fp16,
+            pin_fp8_error_terms]
 
 ALL_PINS = [pin_library_reference, pin_torch_sdpa, pin_identical_keys, pin_first_causal_row,
             pin_scale_zero, pin_key_shift, pin_value_shift, pin_key_permutation, pin_empty_rows,

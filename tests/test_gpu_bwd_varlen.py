@@ -128,3 +128,9 @@ def test_bwd_varlen_skips_malformed_sequences(dev, oracle_lib):
     keep = np.r_[0:s1, e1:q.shape[0]]
     parity.check_grads((dq[keep], dk[keep], dv[keep]), (rq[keep], rk[keep], rv[keep]), F16,
                        "bwd varlen other sequences")
+    # gradients allocated by the binding start at zero
+    g2 = fa.bwd_varlen(qd, kd, vd, o, lse, gd, cqd, ckd, 100, 100, causal=True)
+    torch.cuda.synchronize()
+    for t, r, n in zip(g2, (dq, dk, dv), ("dq", "dk", "dv")):
+        assert torch.all(t[s1:e1] == 0), f"binding-allocated {n} not cleared"
+        assert torch.equal(t[keep], r[keep]), f"binding-allocated {n} differs"

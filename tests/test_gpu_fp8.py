@@ -7,14 +7,18 @@ against the fp64 FP8 oracle (oracle/fp8.py).
   integer and, at scale = 1/log2(e), every lifted weight 2^(s - M + 4) is a
   power of two that e4m3 holds exactly.  Rounding P then loses nothing and the
   output must match the oracle to bf16 output rounding (2^-8 of max |O|).
-* Random cases (inputs quantized by the oracle's quantizer on the CPU): P's
-  rounding to e4m3 is bounded per element by
+* Random cases and long_causal (inputs quantized by the oracle's quantizer on
+  the CPU): P's rounding to e4m3 is checked two ways (tests/fp8_check.py): a
+  worst-case bound per element,
       |dO_t| <= 2^-4 A_t + 2^-14 U_t + 2^-8 |O_t| + 1e-5 A_t
   with A_t = sum_j w_j |v_jt| and U_t the |v| mass of weights below 2^-10 of
   the row maximum (unit roundoff 2^-4 of e4m3 normals; below 2^-6 in the
   lifted units, where the largest weight is at least 2^4, the spacing is 2^-9;
-  bf16 output rounding; fp32 accumulation).  The LSE does not see P's rounding
-  and keeps the 1e-4 bar.
+  bf16 output rounding; fp32 accumulation), and a statistical bound over all
+  compared elements (mean z^2 <= 1 with z the error over the spread of
+  independent round-to-nearest errors), which fails for O = 0 or a dropped V
+  scale where the worst-case bound alone would not.  The LSE does not see P's
+  rounding and keeps the 1e-4 bar.
 """
 import math
 
@@ -25,6 +29,7 @@ import torch
 from exact_attention_22_amd import fa
 from exact_attention_22_amd.inputs import BY_NAME, make_qkv
 from oracle import fp8 as ofp8
+from tests import fp8_check
 
 pytestmark = pytest.mark.gpu
 F16, BF16 = torch.float16, torch.bfloat16
@@ -166,24 +171,15 @@ def test_fwd_fp8_random(dev, case):
     scale = 1 / math.sqrt(d)
     say(f"fa_fwd_fp8 random {case}")
     o, lse = run_fp8(dev, q8, k8, v8, qd, kd, vd, causal, scale)
-    ro, rl, A, U = ofp8.attention_fp8(q8, k8, v8, qd, kd, vd, causal, scale)
-    check_bound(o, ro, A, U, f"random {case}")
+    ro, rl, A, U, R = ofp8.attention_fp8(q8, k8, v8, qd, kd, vd, causal, scale, spread=True)
+    fp8_check.check(o.double().cpu().numpy(), ro, A, U, R, f"random {case}")
     check_lse(lse, rl, f"random {case}")
-
-
-def check_bound(o, ro, A, U, what):
-    a = o.double().cpu().numpy().reshape(ro.shape)
-    assert not np.isnan(a).any(), f"{what}: NaN in O"
-    bound = 2.0 ** -4 * A + 2.0 ** -14 * U + 2.0 ** -8 * np.abs(ro) + 1e-5 * A + 1e-7
-    ratio = np.abs(a - ro) / bound
-    print(f"[parity] {what} max|dO|={np.max(np.abs(a - ro)):.3e} worst ratio to bound={ratio.max():.3f} "
-          f"mean|dO|/mean A={np.mean(np.abs(a - ro)) / max(np.mean(A), 1e-30):.2e}", flush=True)
-    assert ratio.max() <= 1.0, f"{what}: O outside the e4m3 rounding bound (ratio {ratio.max():.3f})"
 
 
 def test_fwd_fp8_long_causal_sampled(dev):
     """long_causal's shapes (B=1 H=32 N=8192 d=128 causal) quantized on the CPU
-    by the oracle's quantizer; sampled rows of the first and last heads."""
+    by the oracle's quantizer; the first, second and last rows of every head and
+    eight seeded random rows per head (352 rows, 45,056 outputs)."""
     w = BY_NAME["long_causal"]
     q, k, v = make_qkv(w)
     G = w.B * w.H
@@ -196,10 +192,10 @@ def test_fwd_fp8_long_causal_sampled(dev):
     say("fa_fwd_fp8 long_causal")
     o, lse = run_fp8(dev, q8, k8, v8, qd, kd, vd, True, w.scale)
     rng = np.random.default_rng(5)
-    heads = np.array([0, G - 1])
-    rows = np.unique(np.concatenate([heads * w.Nq, heads * w.Nq + w.Nq - 1,
-                                     heads[rng.integers(0, 2, 64)] * w.Nq + rng.integers(0, w.Nq, 64)]))
-    ro, rl, A, U = ofp8.attention_fp8(q8, k8, v8, qd, kd, vd, True, w.scale, rows=rows)
+    heads = np.arange(G)
+    rows = np.unique(np.concatenate([heads * w.Nq, heads * w.Nq + 1, heads * w.Nq + w.Nq - 1,
+                                     np.repeat(heads, 8) * w.Nq + rng.integers(0, w.Nq, 8 * G)]))
+    ro, rl, A, U, R = ofp8.attention_fp8(q8, k8, v8, qd, kd, vd, True, w.scale, rows=rows, spread=True)
     idx = torch.from_numpy(rows).to(dev)
-    check_bound(o.reshape(-1, w.d)[idx], ro, A, U, "long_causal sampled")
+    fp8_check.check(o.reshape(-1, w.d)[idx].double().cpu().numpy(), ro, A, U, R, "long_causal sampled")
     check_lse(lse.reshape(-1)[idx], rl, "long_causal sampled")

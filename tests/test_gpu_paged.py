@@ -90,6 +90,12 @@ def test_paged_bad_entries(dev, oracle_lib):
     r1o, r1l = oracle_lib.attention_paged(q[1:2].contiguous(), kc, vc, bt1, [64], scale)
     parity.check(o.reshape(2, H, d), lse.reshape(2, H), np.concatenate([r0o, r1o]), np.concatenate([r0l, r1l]),
                  w.dtype, "paged decode with dropped pages")
+    # partials allocated by the binding start as empty splits: the skipped
+    # sequence combines to O = 0, LSE = -inf instead of uninitialised memory
+    o3, l3 = fa.decode_paged(q.to(dev), kc.to(dev), vc.to(dev), bt_bad.to(dev), sl_bad.to(dev), num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.all(o3[2] == 0) and torch.all(torch.isneginf(l3[2])), "skipped sequence not empty"
+    assert torch.equal(o3[:2], o.reshape(o3[:2].shape)) and torch.equal(l3[:2], lse.reshape(l3[:2].shape))
 
 
 def test_decode_paged_workload(dev, oracle_lib):

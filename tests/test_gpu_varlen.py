@@ -116,6 +116,12 @@ def test_varlen_skips_malformed_sequences(dev, oracle_lib):
     assert torch.all(out[s1:e1] == 7.0) and torch.all(lse[:, s1:e1] == 7.0), "skipped rows were written"
     keep = np.r_[0:s1, e1:q.shape[0]]
     parity.check(out[keep], lse[:, keep].T, ro[keep], rl[:, keep].T, F16, "varlen other sequences")
+    # outputs allocated by the binding start as O = 0, LSE = -inf, so a skipped
+    # sequence reads as one that sees no key instead of uninitialised memory
+    o2, l2 = fa.fwd_varlen(q.to(dev), k.to(dev), v.to(dev), cq.to(dev), ck.to(dev), 100, 100, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(o2[s1:e1] == 0) and torch.all(torch.isneginf(l2[:, s1:e1])), "binding outputs not cleared"
+    assert torch.equal(o2[keep], out[keep]) and torch.equal(l2[:, keep], lse[:, keep])
 
 
 def test_varlen_gqa_workload(dev, oracle_lib):

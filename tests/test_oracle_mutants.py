@@ -142,6 +142,18 @@ FP8_MUTANTS = {
     # attention: causal bound off by one
     "causal": ("hi = Nk if not causal else max(0, min(Nk, i + (Nk - Nq) + 1))",
                "hi = Nk if not causal else max(0, min(Nk, i + (Nk - Nq)))"),
+    # error terms: U weighted by the small weights instead of counting their |v|
+    "u_weighted": ("umag[r] = np.abs(vx[:hi])[p < 2.0 ** -10].sum(axis=0) / l",
+                   "umag[r] = (p[p < 2.0 ** -10] @ np.abs(vx[:hi])[p < 2.0 ** -10]) / l"),
+    # error terms: subnormal threshold 2^-9 instead of 2^-10
+    "u_threshold": ("umag[r] = np.abs(vx[:hi])[p < 2.0 ** -10].sum(axis=0) / l",
+                    "umag[r] = np.abs(vx[:hi])[p < 2.0 ** -9].sum(axis=0) / l"),
+    # error terms: A without the absolute value of v
+    "a_signed": ("amag[r] = (p @ np.abs(vx[:hi])) / l", "amag[r] = (p @ vx[:hi]) / l"),
+    # error terms: R without the absolute floor of the smallest weights
+    "r_no_floor": ("e = np.maximum(2.0 ** -4 * p, 2.0 ** -14)", "e = 2.0 ** -4 * p"),
+    # error terms: R summed linearly instead of in quadrature
+    "r_linear": ("rms[r] = np.sqrt((e * e) @ (vx[:hi] * vx[:hi])) / l", "rms[r] = (e @ np.abs(vx[:hi])) / l"),
 }
 
 
