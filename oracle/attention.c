@@ -74,8 +74,24 @@ double oracle_decode_bf16(uint16_t b) {
     return sign ? -mag : mag;
 }
 
+/* Every 16-bit pattern decoded once by the functions above, so that the inner
+ * products below read a table instead of re-decoding: the values are the same
+ * doubles either way. */
+static double f16_values[65536], bf16_values[65536];
+static pthread_once_t values_once = PTHREAD_ONCE_INIT;
+
+static void fill_values(void) {
+    for (uint32_t x = 0; x < 65536; ++x) {
+        f16_values[x] = oracle_decode_f16((uint16_t)x);
+        bf16_values[x] = oracle_decode_bf16((uint16_t)x);
+    }
+}
+
+/* called by every entry point that decodes, before any worker starts */
+static void ensure_values(void) { pthread_once(&values_once, fill_values); }
+
 static double decode(uint16_t x, int dtype) {
-    return dtype == ORACLE_BF16 ? oracle_decode_bf16(x) : oracle_decode_f16(x);
+    return dtype == ORACLE_BF16 ? bf16_values[x] : f16_values[x];
 }
 
 typedef struct {
@@ -210,6 +226,7 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
     if (!q || !k || !v || !o || !lse) return -1;
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || nrows < 0) return -1;
     if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    ensure_values();
     const int64_t total = (int64_t)B * H * Nq;
     if (!rows && nrows != total) return -1;
     if (rows)
@@ -234,6 +251,7 @@ int oracle_attention_varlen(const uint16_t *q, const uint16_t *k, const uint16_t
     if (!q || !k || !v || !o || !lse || !cu_q || !cu_k) return -1;
     if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || d <= 0 || nrows < 0) return -1;
     if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    ensure_values();
     if (cu_q[0] != 0 || cu_k[0] != 0) return -1;
     int max_k = 0;
     for (int b = 0; b < B; ++b) {
@@ -321,8 +339,10 @@ int oracle_combine(const double *o_part, const double *lse_part, int S, int64_t 
  * with the scores here S = sigma * Q K^T, so the chain rule adds sigma to dQ and
  * dK (dS is the gradient with respect to the scaled scores).  Masked keys have
  * P = 0 and so contribute nothing; a row that sees no key has P = 0 throughout.
- * The statistics of every query row of the (b, h) heads that are needed are
- * computed first (m, l and D_i = rowsum(dP o P)); then
+ * The statistics of the query rows that the requested gradients read are
+ * computed first (m, l and D_i = rowsum(dP o P)): each requested query row, and
+ * for a head with requested key rows every query row that sees one of them
+ * (causal: rows i >= j_min - (Nk - Nq); otherwise all rows); then
  *   dq_i = sigma * sum_j dS_ij k_j                 for the requested query rows,
  *   dv_j = sum_i P_ij dO_i,  dk_j = sigma * sum_i dS_ij q_i   for the requested key rows.
  * Layouts [B, H, N, d]; q_rows are flat (b*H + h)*Nq + i, k_rows (b*H + h)*Nk + j;
@@ -340,6 +360,7 @@ typedef struct {
     int64_t first, last;        /* worker's slice: phase 0 rows of needed heads, 1 q rows, 2 k rows */
     int phase;
     const int64_t *stat_rows;   /* phase 0: flat query rows needing statistics */
+    int failed;                 /* set by a worker that could not allocate */
 } bjob_t;
 
 static int row_visible_end(int i, int Nq, int Nk, int causal) {
@@ -355,7 +376,8 @@ static double dot_rows(const uint16_t *a, const uint16_t *b, int d, int dtype) {
     return acc;
 }
 
-static void bwd_stats(const bjob_t *jb, int64_t flat) {
+/* s: scratch of Nk doubles for the row's scaled scores */
+static void bwd_stats(const bjob_t *jb, int64_t flat, double *s) {
     const int d = jb->d, Nq = jb->Nq, Nk = jb->Nk;
     const int64_t bh = flat / Nq;
     const int i = (int)(flat % Nq);
@@ -367,14 +389,14 @@ static void bwd_stats(const bjob_t *jb, int64_t flat) {
     const int hi = row_visible_end(i, Nq, Nk, jb->causal);
     double m = -INFINITY;
     for (int j = 0; j < hi; ++j) {
-        double s = jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype);
-        if (s > m) m = s;
+        s[j] = jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype);
+        if (s[j] > m) m = s[j];
     }
     double l = 0.0;
-    for (int j = 0; j < hi; ++j) l += exp(jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype) - m);
+    for (int j = 0; j < hi; ++j) l += exp(s[j] - m);
     double D = 0.0;                                           /* rowsum(dP o P) */
     for (int j = 0; j < hi; ++j) {
-        double p = exp(jb->sigma * dot_rows(qi, kp + (size_t)j * d, d, jb->dtype) - m) / l;
+        double p = exp(s[j] - m) / l;
         D += p * dot_rows(gi, vp + (size_t)j * d, d, jb->dtype);
     }
     jb->m[slot] = m;
@@ -424,15 +446,22 @@ static void bwd_k_row(const bjob_t *jb, int64_t flat, double *dk, double *dv) {
 
 static void *bwd_worker(void *arg) {
     bjob_t *jb = (bjob_t *)arg;
+    double *s = NULL;
+    if (jb->phase == 0 && jb->last > jb->first) {
+        s = (double *)malloc(sizeof(double) * (size_t)jb->Nk);
+        if (!s) { jb->failed = 1; return NULL; }
+    }
     for (int64_t r = jb->first; r < jb->last; ++r) {
-        if (jb->phase == 0) bwd_stats(jb, jb->stat_rows[r]);
+        if (jb->phase == 0) bwd_stats(jb, jb->stat_rows[r], s);
         else if (jb->phase == 1) bwd_q_row(jb, jb->q_rows ? jb->q_rows[r] : r, jb->dq + r * jb->d);
         else bwd_k_row(jb, jb->k_rows ? jb->k_rows[r] : r, jb->dk + r * jb->d, jb->dv + r * jb->d);
     }
+    free(s);
     return NULL;
 }
 
-static void bwd_run(const bjob_t *base, int phase, int64_t n, int nthreads) {
+/* Returns 0, or -2 if a worker could not allocate its scratch. */
+static int bwd_run(const bjob_t *base, int phase, int64_t n, int nthreads) {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if ((int64_t)nthreads > n) nthreads = n > 0 ? (int)n : 1;
@@ -447,8 +476,12 @@ static void bwd_run(const bjob_t *base, int phase, int64_t n, int nthreads) {
         started[w] = pthread_create(&tid[w], NULL, bwd_worker, &jobs[w]) == 0;
         if (!started[w]) bwd_worker(&jobs[w]);
     }
-    for (int w = 0; w < nthreads; ++w)
+    int rc = 0;
+    for (int w = 0; w < nthreads; ++w) {
         if (started[w]) pthread_join(tid[w], NULL);
+        if (jobs[w].failed) rc = -2;
+    }
+    return rc;
 }
 
 int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
@@ -458,6 +491,7 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || n_q < 0 || n_k < 0) return -1;
     if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    ensure_values();
     const int64_t BH = (int64_t)B * H;
     if (!q_rows && n_q != BH * Nq) return -1;
     if (!k_rows && n_k != BH * Nk) return -1;
@@ -478,20 +512,53 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
         int64_t h = (k_rows ? k_rows[r] : r) / Nk;
         if (slot[h] < 0) slot[h] = nheads++;
     }
-    const int64_t nstat = nheads * Nq;
-    double *m = (double *)malloc(sizeof(double) * (size_t)(nstat > 0 ? nstat : 1));
-    double *l = (double *)malloc(sizeof(double) * (size_t)(nstat > 0 ? nstat : 1));
-    double *D = (double *)malloc(sizeof(double) * (size_t)(nstat > 0 ? nstat : 1));
-    int64_t *srows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nstat > 0 ? nstat : 1));
-    if (!m || !l || !D || !srows) { free(slot); free(m); free(l); free(D); free(srows); return -2; }
-    for (int64_t h = 0, n = 0; h < BH; ++h)
+    const int64_t nslots = nheads * Nq;
+    double *m = (double *)malloc(sizeof(double) * (size_t)(nslots > 0 ? nslots : 1));
+    double *l = (double *)malloc(sizeof(double) * (size_t)(nslots > 0 ? nslots : 1));
+    double *D = (double *)malloc(sizeof(double) * (size_t)(nslots > 0 ? nslots : 1));
+    int64_t *srows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nslots > 0 ? nslots : 1));
+    char *need = (char *)calloc((size_t)(nslots > 0 ? nslots : 1), 1);
+    if (!m || !l || !D || !srows || !need) {
+        free(slot); free(m); free(l); free(D); free(srows); free(need);
+        return -2;
+    }
+    /* rows whose statistics a requested gradient reads: the requested query rows,
+     * and every query row that sees a requested key (key j is seen by query i
+     * iff j < row_visible_end(i), i.e. causal: i >= j - (Nk - Nq)) */
+    for (int64_t r = 0; r < n_q; ++r) {
+        const int64_t f = q_rows ? q_rows[r] : r;
+        need[slot[f / Nq] * Nq + f % Nq] = 1;
+    }
+    int *first = (int *)malloc(sizeof(int) * (size_t)(nheads > 0 ? nheads : 1));   /* per slot */
+    if (!first) {
+        free(slot); free(m); free(l); free(D); free(srows); free(need);
+        return -2;
+    }
+    for (int64_t h = 0; h < nheads; ++h) first[h] = Nq;
+    for (int64_t r = 0; r < n_k; ++r) {
+        const int64_t f = k_rows ? k_rows[r] : r;
+        const int j = (int)(f % Nk);
+        int lo = causal ? j - (Nk - Nq) : 0;
+        if (lo < 0) lo = 0;
+        if (lo < first[slot[f / Nk]]) first[slot[f / Nk]] = lo;
+    }
+    for (int64_t h = 0; h < nheads; ++h)
+        for (int i = first[h]; i < Nq; ++i) need[h * Nq + i] = 1;
+    free(first);
+    int64_t nstat = 0;
+    for (int64_t h = 0; h < BH; ++h)
         if (slot[h] >= 0)
-            for (int i = 0; i < Nq; ++i) srows[slot[h] * Nq + i] = h * Nq + i, ++n;
+            for (int i = 0; i < Nq; ++i) {
+                const int64_t sl = slot[h] * Nq + i;
+                m[sl] = l[sl] = D[sl] = NAN;          /* never read unless computed */
+                if (need[sl]) srows[nstat++] = h * Nq + i;
+            }
+    free(need);
     bjob_t base = {q, k, v, dout, dtype, H, Nq, Nk, d, causal, (double)scale, m, l, D, slot,
-                   q_rows, k_rows, n_q, n_k, dq, dk, dv, 0, 0, 0, srows};
-    bwd_run(&base, 0, nstat, nthreads);
-    bwd_run(&base, 1, n_q, nthreads);
-    bwd_run(&base, 2, n_k, nthreads);
+                   q_rows, k_rows, n_q, n_k, dq, dk, dv, 0, 0, 0, srows, 0};
+    int rc = bwd_run(&base, 0, nstat, nthreads);
+    if (rc == 0) rc = bwd_run(&base, 1, n_q, nthreads);
+    if (rc == 0) rc = bwd_run(&base, 2, n_k, nthreads);
     free(slot); free(m); free(l); free(D); free(srows);
-    return 0;
+    return rc;
 }

@@ -4,8 +4,9 @@ the fp64 oracle.
 The library's own forward supplies o and lse (the intended use); the oracle
 computes exact gradients from q, k, v and dout alone.  Small shapes (several
 tiles, ragged tails, Nq != Nk, rows that see no key, a single query row) are
-compared on every element; the causal_d128 workload and a grouped-head causal
-prefill are compared at full size on sampled query and key rows.
+compared on every element; the causal_d128 workload, a grouped-head causal
+prefill and the benchmark's long_causal backward are compared at full size on
+sampled query and key rows.
 """
 import math
 
@@ -158,3 +159,29 @@ def test_bwd_gqa_workload(dev, oracle_lib):
     qi, ki = torch.from_numpy(qr).to(dev), torch.from_numpy(kr).to(dev)
     parity.check_grads((dq.reshape(-1, d)[qi], dk.reshape(-1, d)[ki], dv.reshape(-1, d)[ki]),
                        (rq, rk, rv), dt, "bwd gqa H32/8 N4096 sampled")
+
+
+def test_bwd_long_causal_benchmark_shape(dev, oracle_lib):
+    """The backward the benchmark times: long_causal (B=1 H=32 N=8192 d=128 bf16
+    causal, inputs N(0,1) x 0.5), dO ~ N(0,1), o and lse from fa_fwd.  Rows from
+    all 32 heads: 8 random query rows and the last query row per head (dQ); for
+    dK and dV the last key and 2 random keys among the last 1024 per head, plus
+    keys near the start of 4 heads, whose gradients sum over almost every query
+    row (the oracle needs the statistics of every query row that sees a key)."""
+    w = BY_NAME["long_causal"]
+    q, k, v = make_qkv(w)
+    g = rnd(tuple(q.shape), w.dtype, 19)
+    say(f"fa_bwd {w.name} (the benchmark's shape)")
+    dq, dk, dv = run(dev, q, k, v, g, w.causal, scale=w.scale)
+    G = w.B * w.H
+    heads = np.arange(G)
+    rng = np.random.default_rng(23)
+    qr = np.unique(np.concatenate([heads * w.Nq + w.Nq - 1, np.repeat(heads, 8) * w.Nq + rng.integers(0, w.Nq, 8 * G)]))
+    early = np.array([0 * w.Nk + 0, 9 * w.Nk + 5, 20 * w.Nk + 3000, 31 * w.Nk + 129])
+    kr = np.unique(np.concatenate([heads * w.Nk + w.Nk - 1, early,
+                                   np.repeat(heads, 2) * w.Nk + w.Nk - 1 - rng.integers(0, 1024, 2 * G)]))
+    say(f"oracle bwd {len(qr)} query rows, {len(kr)} key rows")
+    rq, rk, rv = oracle_lib.attention_bwd(q, k, v, g, w.causal, w.scale, q_rows=qr, k_rows=kr)
+    qi, ki = torch.from_numpy(qr).to(dev), torch.from_numpy(kr).to(dev)
+    parity.check_grads((dq.reshape(-1, w.d)[qi], dk.reshape(-1, w.d)[ki], dv.reshape(-1, w.d)[ki]),
+                       (rq, rk, rv), w.dtype, f"bwd {w.name} (all 32 heads sampled)")

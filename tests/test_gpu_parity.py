@@ -1,8 +1,11 @@
 """GPU parity: the HIP library through its C ABI against the fp64 oracle.
 
 Small shapes (several tiles plus ragged tails) are compared on every output
-element; the five named workloads are compared at full size on sampled rows,
-through the same calls the benchmark times.
+element; the named workloads are compared at full size through the same calls
+the benchmark times (every row of the tiny, prefill_d64, causal_d128 and
+decode workloads; four whole heads and samples of every other head of
+long_causal).  Two invariants of the method are checked on the GPU without the
+oracle: key-shift invariance and value-shift equivariance.
 """
 import math
 
@@ -107,6 +110,20 @@ def test_fwd_deterministic_and_in_bounds(dev):
     assert torch.equal(o, o2) and torch.equal(l, l2), "two runs differ"
 
 
+# Rows compared per prefill workload: every row of tiny, prefill_d64 and
+# causal_d128; for long_causal four whole heads (0, 11, 22, 31: 32,768 rows) plus
+# the first, last and 16 seeded random rows of every other head.
+LONG_HEADS = (0, 11, 22, 31)
+
+
+def long_causal_rows(w):
+    rng = np.random.default_rng(17)
+    whole = [np.arange(h * w.Nq, (h + 1) * w.Nq) for h in LONG_HEADS]
+    rest = np.array([h for h in range(w.B * w.H) if h not in LONG_HEADS])
+    some = [rest * w.Nq, rest * w.Nq + w.Nq - 1, np.repeat(rest, 16) * w.Nq + rng.integers(0, w.Nq, 16 * rest.size)]
+    return np.unique(np.concatenate(whole + some))
+
+
 @pytest.mark.parametrize("w", [w for w in WORKLOADS if not w.splits and not w.H_kv and not w.seqlens], ids=lambda w: w.name)
 def test_workload_prefill(dev, oracle_lib, w):
     say(f"workload {w.name} inputs")
@@ -114,15 +131,74 @@ def test_workload_prefill(dev, oracle_lib, w):
     say(f"workload {w.name} fa_fwd")
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
-    rows = None if w.B * w.H * w.Nq <= 4096 else parity.sample_rows(w.B, w.H, w.Nq)
+    rows = long_causal_rows(w) if w.name == "long_causal" else None
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    say(f"workload {w.name} oracle ({'all' if rows is None else len(rows)} rows)")
     ro, rl = oracle_lib.attention(qc, kc, vc, w.causal, w.scale, rows=rows)
     if rows is None:
-        parity.check(o, lse, ro, rl, w.dtype, w.name)
+        parity.check(o, lse, ro, rl, w.dtype, f"{w.name} (every row)")
     else:
         idx = torch.from_numpy(rows)
         parity.check(o.reshape(-1, w.d).cpu()[idx], lse.reshape(-1).cpu()[idx], ro, rl, w.dtype,
-                     f"{w.name} ({len(rows)} sampled rows)")
+                     f"{w.name} ({len(rows)} rows: {len(LONG_HEADS)} whole heads + samples of the rest)")
+
+
+def grid(shape, step, lo, hi, seed, dtype):
+    """Values on a grid of `step` in [lo, hi], exact in fp16 and bf16 here."""
+    g = torch.Generator().manual_seed(seed)
+    n = torch.randint(int(round(lo / step)), int(round(hi / step)) + 1, shape, generator=g)
+    return (n.double() * step).to(dtype)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_key_shift_invariance(dev, dt, causal):
+    """Adding one vector u to every key adds sigma q_i.u to every score of row i:
+    O is unchanged and LSE_i moves by exactly sigma q_i.u (Ringi, "Lecture 25",
+    section 2.1: softmax is invariant to a per-row constant).  Queries are
+    positive and u = 16 in every coordinate, so the shift is about +100 per row
+    and exp of an unshifted score would overflow fp32: the maximum subtraction
+    is exercised.  Keys and u lie on a grid of 1/8, so K + u is exact."""
+    B, H, N, d = 1, 2, 777, 128
+    q = grid((B, H, N, d), 1 / 8, 0.0, 1.5, 61, dt)
+    k = grid((B, H, N, d), 1 / 8, -2.0, 2.0, 62, dt)
+    v = rnd((B, H, N, d), dt, 63)
+    ks = (k.double() + 16.0).to(dt)
+    assert torch.equal(ks.double(), k.double() + 16.0), "shifted keys must be exact"
+    scale = 1 / math.sqrt(d)
+    say(f"key shift invariance causal={causal} {dt}")
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+    o2, lse2 = fa.fwd(q.to(dev), ks.to(dev), v.to(dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    shift = float(np.float32(scale)) * 16.0 * q.double().sum(-1)
+    assert shift.min().item() > 89, "the shift must exceed exp's fp32 range (e^89 > 3.4e38)"
+    do = (o2.double() - o.double()).abs().max().item()
+    dl = ((lse2.double().cpu() - lse.double().cpu() - shift).abs() / lse2.double().cpu().abs().clamp(min=1)).max().item()
+    print(f"[parity] key shift {dt} causal={causal} max|dO|={do:.3e} max rel dLSE={dl:.3e}", flush=True)
+    assert do <= parity.O_TOL[dt], f"O changed by {do:.3e} under a key shift"
+    assert dl <= parity.LSE_TOL, f"LSE moved by the wrong amount ({dl:.3e})"
+
+
+@pytest.mark.parametrize("dt", [F16, BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_value_shift_equivariance(dev, dt, causal):
+    """O(V + 1 w^T) = O(V) + w^T, since each row's weights sum to one; LSE does
+    not change.  V and w lie on a grid of 1/8 in [-2, 2] and [-1, 1], so V + w is
+    exact."""
+    B, H, N, d = 2, 1, 555, 64
+    q, k = rnd((B, H, N, d), dt, 71), rnd((B, H, N, d), dt, 72)
+    v = grid((B, H, N, d), 1 / 8, -2.0, 2.0, 73, dt)
+    wv = grid((1, 1, 1, d), 1 / 8, -1.0, 1.0, 74, dt)
+    vs = (v.double() + wv.double()).to(dt)
+    assert torch.equal(vs.double(), v.double() + wv.double()), "shifted values must be exact"
+    say(f"value shift equivariance causal={causal} {dt}")
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    o2, lse2 = fa.fwd(q.to(dev), k.to(dev), vs.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    do = (o2.double().cpu() - o.double().cpu() - wv.double()).abs().max().item()
+    print(f"[parity] value shift {dt} causal={causal} max|dO - w|={do:.3e}", flush=True)
+    assert do <= parity.O_TOL[dt], f"O(V + w) - O(V) differs from w by {do:.3e}"
+    assert torch.equal(lse, lse2), "LSE must not depend on V"
 
 
 def test_workload_decode(dev, oracle_lib):
