@@ -2,9 +2,13 @@
 //
 // Every entry point validates its arguments on the host before any HIP call,
 // then enqueues its kernels on the caller's stream and returns.  The library
-// allocates, frees and synchronises nothing.
+// allocates, frees and synchronises nothing; fa_bwd_gqa_noalloc keeps its
+// scratch in a fixed device array instead of a caller's workspace.
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -76,6 +80,37 @@ fa_status splitkv_impl(const void* q, const void* k, const void* v, float* o_par
     return from_hip(fa::launch_fwd(p, (hipStream_t)stream));
 }
 
+// Scratch of the no-allocation backward: the backward's fp32 D and lse-in-base-2
+// of up to FA_BWD_NOALLOC_MAX_ROWS query rows.  Each GPU that loads the library
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device array: the kernels get the device address
+// that hipGetSymbolAddress returns on the current device, kept per device.
+constexpr size_t kScratchBytes = (size_t)FA_BWD_NOALLOC_MAX_ROWS * 8u;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_lookup;
+
+// Device address of `scratch` on the current device, looked up on the first call
+// on each device (with that device current) and kept.
+fa_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(scratch_lookup);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,17 +159,28 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
 
 namespace {
 
-fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int H_kv,
-                   int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+// Argument checks of the backward except the workspace (host only, no HIP call).
+fa_status bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+                    fa_dtype dtype) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
     fa_status st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     if ((st = check_heads(H, H_kv)) != FA_OK) return st;
-    if (workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 15u) || ((uintptr_t)workspace & 15u))
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 15u))
         return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int H_kv,
+                   int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+    if (!workspace) return FA_ERR_NULL;
+    fa_status st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15u) return FA_ERR_UNSUPPORTED;
     fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, Nk, d, causal != 0,
                     dtype == FA_BF16, scale, H_kv};
     return from_hip(fa::launch_bwd(p, (hipStream_t)stream));
@@ -155,6 +201,20 @@ fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                      void* stream) {
     return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv, Nq, Nk, d, causal,
                     scale, dtype, stream);
+}
+
+fa_status fa_bwd_gqa_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq,
+                             int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+    fa_status st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
+    if (need == 0 || need > kScratchBytes) return FA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != FA_OK) return st;
+    fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)ws, B, H, Nq, Nk, d, causal != 0,
+                    dtype == FA_BF16, scale, H_kv};
+    return from_hip(fa::launch_bwd(p, (hipStream_t)stream));
 }
 
 fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -18,7 +18,7 @@ FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_bwd_gqa", "fa_bwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
+           "fa_bwd_gqa", "fa_bwd_gqa_noalloc", "fa_bwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
@@ -60,6 +60,8 @@ def lib():
         L.fa_bwd_gqa.restype = i
         L.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, i, f, i,
                                  vp]
+        L.fa_bwd_gqa_noalloc.restype = i
+        L.fa_bwd_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
         L.fa_bwd_varlen.restype = i
         L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                     i, i, i, i, i, i, i, i, i, f, i, vp]
@@ -338,6 +340,27 @@ def _bwd(grouped, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace, s
     else:
         _check(lib().fa_bwd(qp, kp, vp, opp, gp, lp, *ptrs, wp, nws, B, H, Nq, Nk, d, int(bool(causal)),
                             _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
+    return dq, dk, dv
+
+
+BWD_NOALLOC_MAX_ROWS = 1 << 20     # B * H * Nq limit of bwd_gqa_noalloc (FA_BWD_NOALLOC_MAX_ROWS)
+
+
+def bwd_gqa_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, scale=None, stream=None):
+    """fa_bwd_gqa_noalloc: bwd_gqa without a workspace (the library's fixed device
+    scratch holds it), for callers that cannot allocate.  The caller passes the
+    outputs dq, dk, dv; nothing is allocated here either.  B * H * Nq must not
+    exceed BWD_NOALLOC_MAX_ROWS.  Calls overlapping in time on one GPU race."""
+    (qp, kp, vp), (B, H, H_kv, Nq, Nk, d) = _qkv(q, k, v, grouped=True)
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o and dout must be [B, H, Nq, d] and lse [B, H, Nq]")
+    if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(v.shape):
+        raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    opp, gp = _dev_tensor(o, "o", q.dtype), _dev_tensor(dout, "dout", q.dtype)
+    lp = _dev_tensor(lse, "lse", torch.float32)
+    ptrs = [_dev_tensor(t, n, q.dtype) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _check(lib().fa_bwd_gqa_noalloc(qp, kp, vp, opp, gp, lp, *ptrs, B, H, H_kv, Nq, Nk, d, int(bool(causal)),
+                                    _scale(scale, d), _DTYPES[q.dtype], _stream(stream)))
     return dq, dk, dv
 
 

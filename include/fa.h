@@ -293,6 +293,30 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that forbid hipMalloc, harnesses without an allocator):
+ * fa_bwd_gqa without the workspace argument.  The D and lse-in-base-2 values
+ * that fa_bwd_gqa keeps in the caller's workspace live instead in a scratch
+ * array inside the library: FA_BWD_NOALLOC_MAX_ROWS query rows (B * H * Nq) at
+ * 8 bytes each, 8 MiB, held on every GPU the library runs on until the process
+ * ends.  The caller still passes every input and output; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine) and gives the
+ * same results as fa_bwd_gqa bit for bit.  B * H * Nq above the maximum returns
+ * FA_ERR_WORKSPACE before any HIP call.  The first call on a device looks up the
+ * scratch array's address on that device (hipGetSymbolAddress; FA_ERR_HIP if
+ * that fails).  Every call on one GPU uses that GPU's one array: calls that
+ * overlap in time on one GPU (different streams, or host threads) race and
+ * corrupt each other's gradients; calls enqueued on one stream are ordered and
+ * safe.  Nothing in the array needs to start at zero: each call writes every
+ * value it reads.  Other arguments and errors as fa_bwd_gqa.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 20)
+
+fa_status fa_bwd_gqa_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq,
+                             int Nk, int d, int causal, float scale, fa_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

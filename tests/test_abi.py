@@ -122,6 +122,31 @@ def test_bwd_gqa_validation():
     assert bwd_gqa(dv=MIS) == fa.FA_ERR_UNSUPPORTED
 
 
+def bwd_noalloc(q=A, k=A, v=A, o=A, g=A, lse=A, dq=A, dk=A, dv=A, B=2, H=4, H_kv=2, Nq=64, Nk=64, d=128,
+                causal=1, scale=0.1, dtype=1):
+    return fa.lib().fa_bwd_gqa_noalloc(q, k, v, o, g, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d, causal, scale,
+                                       dtype, NULL)
+
+
+def test_bwd_noalloc_validation():
+    """Every bad argument is refused on the host, before the scratch lookup (a HIP
+    call); B * H * Nq beyond the scratch's FA_BWD_NOALLOC_MAX_ROWS rows is
+    FA_ERR_WORKSPACE."""
+    assert bwd_noalloc(lse=NULL) == fa.FA_ERR_NULL
+    assert bwd_noalloc(dq=NULL) == fa.FA_ERR_NULL
+    assert bwd_noalloc(H_kv=3) == fa.FA_ERR_SHAPE
+    assert bwd_noalloc(Nq=0) == fa.FA_ERR_SHAPE
+    assert bwd_noalloc(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_noalloc(dtype=5) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_noalloc(dk=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_noalloc(scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
+    limit = fa.BWD_NOALLOC_MAX_ROWS
+    with open(HEADER) as f:
+        assert f"#define FA_BWD_NOALLOC_MAX_ROWS (1 << {limit.bit_length() - 1})" in f.read()
+    assert bwd_noalloc(B=1, H=32, H_kv=32, Nq=limit // 32 + 1) == fa.FA_ERR_WORKSPACE
+    assert bwd_noalloc(B=2, H=limit // 64, H_kv=1, Nq=33) == fa.FA_ERR_WORKSPACE
+
+
 def bwd_varlen(q=A, k=A, v=A, o=A, g=A, lse=A, dq=A, dk=A, dv=A, cq=A, ck=A, ws=A, wsb=1 << 20, B=2, H=4,
                H_kv=2, total_q=16, total_k=24, max_q=9, max_k=13, d=128, causal=1, scale=0.1, dtype=1):
     return fa.lib().fa_bwd_varlen(q, k, v, o, g, lse, dq, dk, dv, cq, ck, ws, wsb, B, H, H_kv, total_q, total_k,
