@@ -2,12 +2,12 @@
 // partials for any Nq).
 //
 // Method (the pages this follows):
-//   * Q outer, KV inner: one workgroup owns one tile of Br = 128 query rows of
-//     one (b, h) and walks the key tiles; O stays on chip and is written once
+//   * Q outer, KV inner: one workgroup owns one tile of Br = 128 (or 256) query
+//     rows of one (b, h) and walks the key tiles; O stays on chip and is written once
 //     (AIInfraGuide 6.2 "FlashAttention V2 explained", section 2; LLM Infra
 //     Atlas "FA2: parallelism", section 2: grid over query tiles x batch x heads).
-//   * split-Q: each of the 4 wavefronts owns 32 query rows and computes their
-//     whole softmax, so waves never reduce across each other (LLM Infra Atlas,
+//   * split-Q: each wavefront owns 32 query rows and computes their whole
+//     softmax, so waves never reduce across each other (LLM Infra Atlas,
 //     section 3; AIInfraGuide 6.2, section 4).
 //   * online softmax with an unnormalised accumulator: O <- alpha*O + P V and
 //     l <- alpha*l + rowsum(P), divided by l once at the end (Ringi, "Lecture 25",
@@ -40,15 +40,21 @@
 //   * Lazy rescale: the exponent reference only moves (and O, l are only
 //     rescaled) when it would let a weight grow too large, decided per
 //     wavefront.  Any reference gives the same O = sum 2^(t-M) v / sum 2^(t-M).
-//     Tiles that cross the diagonal or the key tail take the row maximum and
-//     move the reference when it is exceeded by more than 2^8 in probability.
-//     Fully visible tiles skip the maximum: each 32-key block is exponentiated
-//     against the current reference and kept when every lane's sum of its 16
-//     weights stays <= 2^12; otherwise the reference moves to the block's exact
-//     running maximum and the block is exponentiated again (rescaling between
-//     blocks is the online-softmax merge).  The reference is always an observed
-//     maximum, so it never exceeds the true one; every P stays <= 2^12, far
-//     inside fp16 range.
+//     Each 32-key block is exponentiated against the current reference and kept
+//     when every lane's sum of its 16 weights stays <= 2^12; otherwise the
+//     reference moves to the block's exact running maximum and the block is
+//     exponentiated again (rescaling between blocks is the online-softmax
+//     merge), so no row maximum is taken while the reference holds.  Keys past
+//     the diagonal or the key tail weigh exactly 0.  The reference is always an
+//     observed maximum, so it never exceeds the true one; every P stays <= 2^12,
+//     far inside fp16 range.
+//   * Within a 64-key tile, block 1's S^T products are issued between block
+//     0's softmax instructions, and block 0's P V products between block 1's
+//     (scheduling groups), so a wavefront's vector work runs while its own
+//     products occupy the matrix core.
+//   * A workgroup is 4 wavefronts (128 query rows, two workgroups per CU) or,
+//     over long key ranges, 8 (256 rows, one per CU), which loads each K/V tile
+//     into LDS once for twice the query rows.
 //   * Workgroups are mapped so that consecutive tiles of one head share an XCD
 //     (and its L2).  Causal [B, H, N, d]: one workgroup runs query tiles
 //     n_qtiles-1-t and t, which together see a fixed number of key tiles, so
@@ -63,10 +69,8 @@
 namespace fa {
 namespace {
 
-constexpr int BR = 128;     // query rows per workgroup (4 waves x 32)
 constexpr int BC = 64;      // keys per tile
-constexpr float SUM_CAP = 4096.f;  // fully visible tiles: largest per-lane sum of 16 weights kept
-constexpr float TAU = 8.0f; // lazy-rescale threshold, log2 units
+constexpr float SUM_CAP = 4096.f;  // largest per-lane sum of a block's 16 weights kept without moving the reference
 
 struct FwdArgs {
     const uint16_t* q;
@@ -95,9 +99,12 @@ __device__ __forceinline__ int perm_row(int i) {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+// NW wavefronts per workgroup, 32 query rows each: 4 (two workgroups per CU) or 8
+// (one per CU; each K/V tile is then loaded once for 256 query rows)
+template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool VARLEN, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
     static_assert(!(SPLIT && VARLEN), "split-KV partials take the [B,H,N,d] layout");
+    constexpr int BR = 32 * NW;                  // query rows per workgroup
     constexpr int ROWB = D * 2;                  // bytes per K/V row
     constexpr int TILE = BC * ROWB;              // bytes per K (or V) tile
     constexpr int NS = D / 16;                   // 16-wide d slices of Q
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         // that position (global rows are kv_rowb bytes apart); these offsets do not
         // change from tile to tile.  Reads past the sequence's last key return zeros
         // (the descriptor's record count ends with that key's row).
-        constexpr int NPW = TILE / 1024 / 4;         // 1 KiB loads per wave per tensor per tile
+        constexpr int NPW = TILE / 1024 / NW;        // 1 KiB loads per wave per tensor per tile
         u32 voff[NPW];
     #pragma unroll
         for (int u = 0; u < NPW; ++u) {
@@ -203,6 +210,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         auto load_half = [&](int tile, unsigned char* stage, int which) {
             const int k0 = ks + tile * BC;
             const u32 nrec = (u32)(min(Nk - k0, BC) - 1) * kv_rowb + ROWB;
+            const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * kv_rs, nrec);
+            unsigned char* dst = stage + which * TILE + w * NPW * 1024;
+    #pragma unroll
+            for (int u = 0; u < NPW; ++u) lds_dma16(r, dst + u * 1024, voff[u]);
+        };
+        auto load_half_if = [&](int tile, unsigned char* stage, int which, bool on) {
+            const int k0 = ks + tile * BC;
+            const u32 nrec = on ? (u32)(min(Nk - k0, BC) - 1) * kv_rowb + ROWB : 0u;
             const __amdgpu_buffer_rsrc_t r = buffer_rsrc((which ? vg : kg) + (size_t)k0 * kv_rs, nrec);
             unsigned char* dst = stage + which * TILE + w * NPW * 1024;
     #pragma unroll
@@ -236,134 +251,129 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         // One key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
         // MASKED tiles cross the chunk end or (causal) the diagonal.  after_s runs
         // once the S^T products are issued.
-        auto tile_step = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag,
-                             auto&& after_s) {
+        // Fully visible tile, exponentiated one 32-key block at a time against the
+        // current reference: block kb is kept when every lane's partial sum of its
+        // 16 weights stays <= 2^12 (so every weight does) and the reference is set;
+        // otherwise the reference moves to the block's exact running maximum (O and
+        // l rescaled first) and the block is exponentiated again.  Rescaling between
+        // blocks is the online-softmax merge itself, so no row maximum is needed
+        // while the reference holds.
+        // masked blocks: register r of block kb holds key k0 + 8h + kofs(kb, r) and
+        // is visible iff kofs < bound; a hidden key weighs exactly 0 (also when the
+        // scale is 0, where its score times the scale is not defined)
+        auto kofs = [](int kb, int r) { return 32 * kb + 16 * (r >> 3) + (r & 7); };
+        auto expo16 = [&](const f32x16& sc, float* pv, float& t0, float& t1, auto masked_tag, int kb, int bound) {
             constexpr bool MASKED = decltype(masked_tag)::value;
-            f32x16 sacc[2];
+            const float Mg = (Mu == -INFINITY) ? 0.f : Mu;
+            t0 = 0.f;
+            t1 = 0.f;
     #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sacc[kb] = f32x16{};
-    #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const u32x4 kf = *(const u32x4*)(Kb + 32 * kb * ROWB + koff[s]);
-                    sacc[kb] = mfma32<BF16>(kf, qf[s], sacc[kb]);
+            for (int r = 0; r < 16; r += 2) {
+                pv[r] = exp2_fast(__builtin_fmaf(sc[r], a.c, -Mg));
+                pv[r + 1] = exp2_fast(__builtin_fmaf(sc[r + 1], a.c, -Mg));
+                if constexpr (MASKED) {
+                    if (kofs(kb, r) >= bound) pv[r] = 0.f;
+                    if (kofs(kb, r + 1) >= bound) pv[r + 1] = 0.f;
                 }
+                t0 += pv[r];
+                t1 += pv[r + 1];
             }
-            after_s();
-            if constexpr (!MASKED) {
-                // Fully visible tile, one 32-key block at a time: exponentiate against
-                // the current reference and keep the block if every lane's partial sum
-                // of its 16 weights stays <= 2^12 (so every weight does) and the
-                // reference is set; otherwise move the reference to the exact running
-                // maximum (rescaling O and l first) and exponentiate the block again.
-                // Rescaling between blocks is the online-softmax merge itself, so no
-                // row maximum is needed while the reference holds.
+        };
+        auto guard = [&](const f32x16& sc, float* pv, float& t0, float& t1, auto masked_tag, int kb, int bound) {
+            if (__ballot(!(t0 + t1 <= SUM_CAP) || Mu == -INFINITY)) {
+                float mx = sc[0];
     #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    float pv[16];
-                    float t0 = 0.f, t1 = 0.f;
-                    auto expo = [&]() {
-                        const float Mg = (Mu == -INFINITY) ? 0.f : Mu;
-                        t0 = 0.f;
-                        t1 = 0.f;
-    #pragma unroll
-                        for (int r = 0; r < 16; r += 2) {
-                            pv[r] = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
-                            pv[r + 1] = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], a.c, -Mg));
-                            t0 += pv[r];
-                            t1 += pv[r + 1];
-                        }
-                    };
-                    expo();
-                    if (__ballot(!(t0 + t1 <= SUM_CAP) || Mu == -INFINITY)) {
-                        float mx = sacc[kb][0];
-    #pragma unroll
-                        for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sacc[kb][r]);
-                        mx = max_halves(mx);
-                        const float Mn = fmaxf(Mu, (mx == -INFINITY) ? -INFINITY : mx * a.c);
-                        const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
-                        lsum *= alpha;
-    #pragma unroll
-                        for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-                        Mu = Mn;
-                        expo();
-                    }
-                    lsum += t0 + t1;
-    #pragma unroll
-                    for (int p = 0; p < 2; ++p) {
-                        const u32x4 pb = {pack2<BF16>(pv[8 * p + 0], pv[8 * p + 1]), pack2<BF16>(pv[8 * p + 2], pv[8 * p + 3]),
-                                          pack2<BF16>(pv[8 * p + 4], pv[8 * p + 5]), pack2<BF16>(pv[8 * p + 6], pv[8 * p + 7])};
-                        const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
-    #pragma unroll
-                        for (int db = 0; db < ND; ++db) {
-                            const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
-                            const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
-                            oacc[db] = mfma32<BF16>(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb, oacc[db]);
-                        }
-                    }
-                }
-                return;
-            }
-            // register r of block kb holds key k0 + 8h + kofs(kb, r); visible iff kofs < bound
-            int bound = 0;
-            if constexpr (MASKED) {
-                bound = ke - k0 - 8 * h;
-                if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
-    #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) sacc[kb][r] = -INFINITY;
-            }
-            // row max over this tile (raw scores), both lane halves
-            float mx = sacc[0][0];
-    #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sacc[0][r]);
-    #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmax_raw(mx, sacc[1][r]);
-            mx = max_halves(mx);
-            const float Mc = (mx == -INFINITY) ? -INFINITY : mx * a.c;
-            if (__ballot(Mc > Mu + TAU)) {          // wave-uniform: move the reference
-                const float Mn = fmaxf(Mu, Mc);
+                for (int r = 1; r < 16; ++r) mx = fmax_raw(mx, sc[r]);
+                mx = max_halves(mx);
+                const float Mn = fmaxf(Mu, (mx == -INFINITY) ? -INFINITY : mx * a.c);
                 const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(Mu - Mn);
                 lsum *= alpha;
     #pragma unroll
                 for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
                 Mu = Mn;
+                expo16(sc, pv, t0, t1, masked_tag, kb, bound);
             }
-            const float Mg = (Mu == -INFINITY) ? 0.f : Mu;   // no -inf - -inf
-            // P = 2^(s*c - M); masked keys weigh exactly 0 (also when scale is 0)
+            lsum += t0 + t1;
+        };
+        auto pack16 = [&](const float* pv, u32x4* pb) {
     #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int p = 0; p < 2; ++p)
+                pb[p] = u32x4{pack2<BF16>(pv[8 * p + 0], pv[8 * p + 1]), pack2<BF16>(pv[8 * p + 2], pv[8 * p + 3]),
+                              pack2<BF16>(pv[8 * p + 4], pv[8 * p + 5]), pack2<BF16>(pv[8 * p + 6], pv[8 * p + 7])};
+        };
+        auto pv_block = [&](const unsigned char* Vb, int kb, const u32x4* pb) {
     #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = exp2_fast(__builtin_fmaf(sacc[kb][r], a.c, -Mg));
-                    if constexpr (MASKED)
-                        if (32 * kb + 16 * (r >> 3) + (r & 7) >= bound) p = 0.f;
-                    sacc[kb][r] = p;
+            for (int p = 0; p < 2; ++p) {
+                const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
+                    oacc[db] = mfma32<BF16>(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb[p], oacc[db]);
                 }
-            // row sum in fp32, before P is rounded to 16 bits
+            }
+        };
+        // One fully visible key tile.  Block 1's S^T products are issued between
+        // block 0's softmax instructions and block 0's P V products between block
+        // 1's, so the wave's own vector work runs while the matrix core is busy.
+        // MASKED tiles cross the chunk end or (causal) the diagonal; their hidden
+        // scores are set to -inf (so a fallback's row maximum ignores them) and their
+        // weights to 0.
+        auto key_tile = [&](const unsigned char* Kb, const unsigned char* Vb, int k0, auto masked_tag,
+                            auto&& after_s) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            int bound = 0;
+            if constexpr (MASKED) {
+                bound = ke - k0 - 8 * h;
+                if (CAUSAL) bound = min(bound, qi + off - k0 - 8 * h + 1);
+            }
+            auto hide = [&](f32x16& sc, int kb) {
+                if constexpr (MASKED)
     #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                    for (int r = 0; r < 16; ++r)
+                        if (kofs(kb, r) >= bound) sc[r] = -INFINITY;
+            };
+            f32x16 s0 = f32x16{}, s1 = f32x16{};
     #pragma unroll
-                for (int r = 0; r < 16; ++r) lsum += sacc[kb][r];
-            // O^T += V^T P^T
+            for (int s = 0; s < NS; ++s)
+                s0 = mfma32<BF16>(*(const u32x4*)(Kb + koff[s]), qf[s], s0);
+            after_s();
     #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int s = 0; s < NS; ++s)
+                s1 = mfma32<BF16>(*(const u32x4*)(Kb + 32 * ROWB + koff[s]), qf[s], s1);
+            hide(s0, 0);
+            float p0[16], t0, t1;
+            expo16(s0, p0, t0, t1, masked_tag, 0, bound);
     #pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const f32x16& P = sacc[kb];
-                    const u32x4 pb = {pack2<BF16>(P[8 * p + 0], P[8 * p + 1]), pack2<BF16>(P[8 * p + 2], P[8 * p + 3]),
-                                      pack2<BF16>(P[8 * p + 4], P[8 * p + 5]), pack2<BF16>(P[8 * p + 6], P[8 * p + 7])};
-                    const unsigned char* vb = Vb + (32 * kb + 16 * p) * ROWB;
+            for (int s = 0; s < NS; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA (block 0)
+            }
+            __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);       // the next tile's V loads
     #pragma unroll
-                    for (int db = 0; db < ND; ++db) {
-                        const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[0][db]));
-                        const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(vb + voffs[1][db]));
-                        const u32x4 va = {l2[0], l2[1], h2[0], h2[1]};
-                        oacc[db] = mfma32<BF16>(va, pb, oacc[db]);
-                    }
-                }
+            for (int s = 0; s < NS; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA (block 1)
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // block 0's softmax
+            }
+            guard(s0, p0, t0, t1, masked_tag, 0, bound);
+            u32x4 pb0[2];
+            pack16(p0, pb0);
+            pv_block(Vb, 0, pb0);
+            hide(s1, 1);
+            float p1[16], u0, u1;
+            expo16(s1, p1, u0, u1, masked_tag, 1, bound);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);       // V reads of the first two products
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);       // block 0's packing
+    #pragma unroll
+            for (int s = 0; s < 2 * ND; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // one MFMA (block 0's P V)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // V reads one product ahead
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);   // block 1's softmax
+            }
+            guard(s1, p1, u0, u1, masked_tag, 1, bound);
+            u32x4 pb1[2];
+            pack16(p1, pb1);
+            pv_block(Vb, 1, pb1);
         };
 
         // Tiles are walked from the last one down.  The first n_masked of them may
@@ -390,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
             const int k0 = ks + tile * BC;
             const bool active = qw < Nq && (!CAUSAL || k0 <= qmax_w + off);
-            if (active) tile_step(cur, cur + TILE, k0, std::true_type{}, [] {});
+            if (active) key_tile(cur, cur + TILE, k0, std::true_type{}, [] {});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
@@ -402,9 +412,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const int tile = n_tiles - 1 - it;
             const bool more = it + 1 < n_tiles;
             if (more) load_half(tile - 1, nxt, 0);
-            tile_step(cur, cur + TILE, ks + tile * BC, std::false_type{}, [&] {
-                if (more) load_half(tile - 1, nxt, 1);
-            });
+            // the V loads sit inside one scheduling region with the products, so they
+            // are issued without a branch (no records: nothing is read past the last tile)
+            key_tile(cur, cur + TILE, ks + tile * BC, std::false_type{},
+                     [&] { load_half_if(more ? tile - 1 : 0, nxt, 1, more); });
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             ++it;
@@ -486,23 +497,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
 }
 
-template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool VARLEN>
+template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool VARLEN, int NW>
 hipError_t launch_t(const FwdArgs& a, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, SPLIT, VARLEN>), dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, SPLIT, VARLEN, NW>), dim3(blocks), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
-// mode: 0 plain [B,H,N,d], 1 split-KV partials, 2 packed variable-length
+// mode: 0 plain [B,H,N,d], 1 split-KV partials, 2 packed variable-length; wide:
+// eight wavefronts per workgroup (plain mode only)
 template <bool BF16, int D>
-hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, int mode, hipStream_t s) {
+hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, int mode, bool wide, hipStream_t s) {
     if (causal) {
-        if (mode == 1) return launch_t<BF16, D, true, true, false>(a, blocks, s);
-        if (mode == 2) return launch_t<BF16, D, true, false, true>(a, blocks, s);
-        return launch_t<BF16, D, true, false, false>(a, blocks, s);
+        if (mode == 1) return launch_t<BF16, D, true, true, false, 4>(a, blocks, s);
+        if (mode == 2) return launch_t<BF16, D, true, false, true, 4>(a, blocks, s);
+        if constexpr (D == 128)
+            if (wide) return launch_t<BF16, D, true, false, false, 8>(a, blocks, s);
+        return launch_t<BF16, D, true, false, false, 4>(a, blocks, s);
     }
-    if (mode == 1) return launch_t<BF16, D, false, true, false>(a, blocks, s);
-    if (mode == 2) return launch_t<BF16, D, false, false, true>(a, blocks, s);
-    return launch_t<BF16, D, false, false, false>(a, blocks, s);
+    if (mode == 1) return launch_t<BF16, D, false, true, false, 4>(a, blocks, s);
+    if (mode == 2) return launch_t<BF16, D, false, false, true, 4>(a, blocks, s);
+    if constexpr (D == 128)
+        if (wide) return launch_t<BF16, D, false, false, false, 8>(a, blocks, s);
+    return launch_t<BF16, D, false, false, false, 4>(a, blocks, s);
 }
 
 }  // namespace
@@ -521,8 +537,15 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     a.BH = p.B * p.H;
     a.c = fabsf(p.scale) * kLog2e;
     a.qsign = p.scale < 0.f ? 0x80008000u : 0u;
-    a.n_qtiles = (p.Nq + BR - 1) / BR;        // varlen: Nq is the longest query sequence
     const bool split = p.num_splits > 0;
+    const int mode = p.varlen ? 2 : (split ? 1 : 0);
+    // Each workgroup loads every K/V tile it attends to once for its query rows,
+    // so over long key ranges 256 query rows per workgroup (eight wavefronts, one
+    // workgroup per CU) halve the K/V traffic into LDS; on shorter ones the
+    // finer grid of 128-row workgroups (two per CU) balances better.
+    const bool wide = mode == 0 && p.d == 128 && p.Nk >= 4096;
+    const int BR = wide ? 256 : 128;
+    a.n_qtiles = (p.Nq + BR - 1) / BR;        // varlen: Nq is the longest query sequence
     const int S = split ? p.num_splits : 1;
     a.split_chunk = split_chunk(p.Nk, S);
     a.cu_q = p.cu_q;
@@ -533,17 +556,16 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     a.total_k = p.total_k;
     a.max_q = p.Nq;
     a.max_k = p.Nk;
-    const int mode = p.varlen ? 2 : (split ? 1 : 0);
     // causal [B,H,N,d]: one workgroup per pair of query tiles (two pairs per
     // workgroup, one dispatch round with no rebalancing, measured slower)
     a.paired = (p.causal && mode == 0 && a.n_qtiles >= 2) || (mode == 2 && (a.B * a.H_kv) % 8 == 0);
     const int64_t blocks = a.paired ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH : (int64_t)a.n_qtiles * a.BH * S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.d == 128)
-        return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, mode, stream)
-                      : dispatch_cs<false, 128>(a, (int)blocks, p.causal, mode, stream);
-    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, mode, stream)
-                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, mode, stream);
+        return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, mode, wide, stream)
+                      : dispatch_cs<false, 128>(a, (int)blocks, p.causal, mode, wide, stream);
+    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, mode, false, stream)
+                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, mode, false, stream);
 }
 
 }  // namespace fa
