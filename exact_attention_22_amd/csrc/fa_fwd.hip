@@ -18,7 +18,8 @@
 //     the diagonal or the key tail are masked, and walking the tiles from the
 //     last one down puts those first (LLM Infra Atlas, section 4; KingOfEgg,
 //     section 3.2).
-//   * epilogue: inv = 1 when the row sum is 0 or NaN; LSE = max*scale + ln(sum)
+//   * epilogue: inv = 1 when the row sum is 0 or NaN; LSE = max*scale + ln(sum);
+//     O is re-laid through shared memory so that the stores cover whole rows
 //     (KingOfEgg, section 3.5).
 //
 // gfx950 mapping (not from the pages):
@@ -444,16 +445,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
                     }
                 if (h == 0) a.lse[((size_t)split * a.BH + bh) * a.Nq + qi] = lse_v;
             } else {
-                uint16_t* op = (uint16_t*)a.o + o0 + (size_t)qi * o_rs;
-    #pragma unroll
-                for (int db = 0; db < ND; ++db)
-    #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const u32x2 v2 = {pack2<BF16>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                                          pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                        *(u32x2*)(op + 32 * db + 8 * g + 4 * h) = v2;
-                    }
                 if (h == 0) lse_g[qi] = lse_v;
+            }
+        }
+        if constexpr (!SPLIT) {
+            // O leaves through LDS: the wave's 32 x D tile is written in the MFMA
+            // layout (8 bytes per lane per block, 16-byte chunks XOR-swizzled by
+            // row) into its own 32-row region of the idle stages, then read back
+            // one 16-byte chunk per lane so that each store covers whole rows.
+            // The last tile ended with a barrier, so no wave still reads the
+            // stages; each wave touches only its own region.
+            constexpr int CH = ROWB / 16;                // 16-byte chunks per row
+            constexpr int RPI = 1024 / ROWB;             // rows per 1 KiB wave access
+            unsigned char* reg = (w < 4 ? stage0 : stage1) + (w & 3) * (32 * ROWB);
+    #pragma unroll
+            for (int db = 0; db < ND; ++db)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2 v2 = {pack2<BF16>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                      pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    const int c = 4 * db + g;
+                    *(u32x2*)(reg + l32 * ROWB + ((c ^ (l32 & (CH - 1))) << 4) + 8 * h) = v2;
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int c = lane % CH;
+    #pragma unroll
+            for (int it2 = 0; it2 < 32 / RPI; ++it2) {
+                const int r = it2 * RPI + lane / CH;
+                const u32x4 v4 = *(const u32x4*)(reg + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+                if (qw + r < Nq) *(u32x4*)((uint16_t*)a.o + o0 + (size_t)(qw + r) * o_rs + 8 * c) = v4;
             }
         }
     };
