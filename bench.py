@@ -22,9 +22,12 @@ the same FLOP convention summed over its sequences.
 
 Each kernel is timed with HIP events recorded on the stream it is launched on;
 every block reports the mean (used for the rooflines), median and minimum over
-the timed steps.  The default run times enough steps for a timed region of a
-few seconds.  The CPU baseline times the fp64 oracle on a bounded sample of
-prefill rows.  Prints one JSON line.
+the timed steps.  A decode's split kernel and its combine are each timed alone
+(the combine queued behind the split kernel), then once more as one unit with
+no marker between them: that unit is the decode line's time.  The default run
+times enough steps for a timed region of a few seconds.  The CPU baseline
+times the fp64 oracle on the prefill rows (all of them by default: about 5 s on
+16 threads).  Prints one JSON line.
 """
 import argparse
 import hashlib

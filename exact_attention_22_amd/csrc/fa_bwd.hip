@@ -27,8 +27,11 @@
 //     S = Q K^T and dP = dO V^T with Q and dO rows in the swapped order, so P and
 //     dS feed dV^T += dO^T P and dK^T += Q^T dS directly.  LSE (in base 2) and
 //     D of the tile's query rows sit in LDS next to the Q and dO tiles.  At one
-//     wave per SIMD the wave overlaps its own work: the scores of a tile's second
-//     32-row block are issued before the first block's element-wise work.
+//     wave per SIMD no other wave hides a wave's LDS latency, so the instruction
+//     order is fixed by scheduling fences: operand reads (above all the
+//     transposed ones) run 8 to 16 reads ahead of their products, the first
+//     block's element-wise work runs beside the second block's scores, and the
+//     second block's beside the first block's gradient products.
 //   * Rows past the end of Q read as zeros (so they add nothing to dK, dV), and
 //     keys past the end of K only reach their own, unstored, dK/dV columns; the
 //     dK/dV kernel therefore only applies the causal condition, as a select per
@@ -438,22 +441,22 @@ __device__ __forceinline__ void dkdv_probs(const f32x16& s, const f32x16& dp, co
     }
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS over those 32 rows.
-template <bool BF16, int D>
-__device__ __forceinline__ void dkdv_accum(const unsigned char* Qb, const unsigned char* Gb, int kb,
-                                           const Offsets<D>& of, const u32x4 (&pb)[2], const u32x4 (&sb)[2],
-                                           f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
-    constexpr int ROWB = D * 2;
+// Four of those rows (register 8p + e0 .. 8p + e0 + 3, e0 in {0, 4}): the same
+// values as dkdv_probs, written into words e0/2, e0/2 + 1 of pb[p] and sb[p].
+template <bool BF16, bool MASK>
+__device__ __forceinline__ void dkdv_probs4(const f32x16& s, const f32x16& dp, const f32x4& l4, const f32x4& d4,
+                                            float c, int lim, int p, int e0, u32x4& pbp, u32x4& sbp) {
+    float pr[4], ds[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const unsigned char* qr = Qb + (32 * kb + 16 * p) * ROWB;
-        const unsigned char* gr = Gb + (32 * kb + 16 * p) * ROWB;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            dv[db] = mfma32<BF16>(tr_operand<D>(gr, of, db), pb[p], dv[db]);
-            dk[db] = mfma32<BF16>(tr_operand<D>(qr, of, db), sb[p], dk[db]);
-        }
+    for (int e = 0; e < 4; ++e) {
+        pr[e] = exp2_fast(__builtin_fmaf(s[8 * p + e0 + e], c, -l4[e]));
+        if (MASK) pr[e] = (16 * p + e0 + e < lim) ? 0.f : pr[e];
+        ds[e] = pr[e] * (dp[8 * p + e0 + e] - d4[e]);
     }
+    pbp[e0 / 2] = pack2<BF16>(pr[0], pr[1]);
+    pbp[e0 / 2 + 1] = pack2<BF16>(pr[2], pr[3]);
+    sbp[e0 / 2] = pack2<BF16>(ds[0], ds[1]);
+    sbp[e0 / 2 + 1] = pack2<BF16>(ds[2], ds[3]);
 }
 
 template <bool BF16, int D, bool CAUSAL, bool VARLEN>
@@ -527,49 +530,142 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const float* Ls = (const float*)(st + 2 * QTILE);
             const float* Ds = (const float*)(st + 2 * QTILE + 1024);
             const int lim = kj - i0 - off - 8 * h;
-            f32x16 s0, d0, s1, d1;
-            u32x4 pb[2], sb[2];
-            // scheduling fences keep the compiler to these four phases
-            scores<BF16, D>(Qb, Gb, 0, of, kf, vf, s0, d0);
-            __builtin_amdgcn_sched_barrier(0);
-            scores<BF16, D>(Qb, Gb, 1, of, kf, vf, s1, d1);
+            constexpr int ROWB = D * 2;
+            // Operand reads are issued in a fixed order (scheduling fences) well ahead of
+            // the products that use them: at one wave per SIMD the LDS latency, above all
+            // of the transposed reads, is not hidden by other waves.
+            auto rows = [&](const unsigned char* T, int kb, int i) {
+                return *(const u32x4*)(T + 32 * kb * ROWB + of.row[i]);
+            };
+            auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+            u32x4 qa[NS], ga[NS], qb[NS], gb[NS];
+    #pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                qa[i] = rows(Qb, 0, i);
+                ga[i] = rows(Gb, 0, i);
+            }
+            fence();
+            // S and dP of rows 0..31, the operands of rows 32..63 read beside them
+            f32x16 s0 = f32x16{}, d0 = f32x16{}, s1 = f32x16{}, d1 = f32x16{};
+    #pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                s0 = mfma32<BF16>(qa[i], kf[i], s0);
+                qb[i] = rows(Qb, 1, i);
+                d0 = mfma32<BF16>(ga[i], vf[i], d0);
+                gb[i] = rows(Gb, 1, i);
+                fence();
+            }
+            // S and dP of rows 32..63 beside the element-wise work of rows 0..31
+            u32x4 pb[2], sb[2], pb1[2], sb1[2];
+    #pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                s1 = mfma32<BF16>(qb[i], kf[i], s1);
+                d1 = mfma32<BF16>(gb[i], vf[i], d1);
+            }
             dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
-            __builtin_amdgcn_sched_barrier(0);
-            dkdv_accum<BF16, D>(Qb, Gb, 0, of, pb, sb, dkacc, dvacc);
-            u32x4 pb1[2], sb1[2];
-            dkdv_probs<BF16, MASK>(s1, d1, Ls, Ds, 32 + 8 * h, a.c, lim - 32, pb1, sb1);
-            __builtin_amdgcn_sched_barrier(0);
-            dkdv_accum<BF16, D>(Qb, Gb, 1, of, pb1, sb1, dkacc, dvacc);
+            fence();
+            // dV^T += dO^T P and dK^T += Q^T dS over one 32-row block: the transposed
+            // operands of its first 16 rows up front, those of the next 16 beside the
+            // first products; `before` runs first, and the four quarters of `beside`
+            // run spread over the products
+            auto accum = [&](int kb, const u32x4 (&pp)[2], const u32x4 (&ss)[2], auto&& before, auto&& beside) {
+                const unsigned char* q0r = Qb + (32 * kb) * ROWB;
+                const unsigned char* g0r = Gb + (32 * kb) * ROWB;
+                before();
+                u32x4 tg[ND], tq[ND], ug[ND], uq[ND];
+                // the 2 ND product pairs carry the four quarters of `beside` evenly
+                auto quarter = [&](int u) {
+                    if (((u + 1) * 4) % (2 * ND) == 0) beside((u + 1) * 4 / (2 * ND) - 1);
+                };
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    tg[db] = tr_operand<D>(g0r, of, db);
+                    tq[db] = tr_operand<D>(q0r, of, db);
+                }
+                fence();
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    dvacc[db] = mfma32<BF16>(tg[db], pp[0], dvacc[db]);
+                    ug[db] = tr_operand<D>(g0r + 16 * ROWB, of, db);
+                    dkacc[db] = mfma32<BF16>(tq[db], ss[0], dkacc[db]);
+                    uq[db] = tr_operand<D>(q0r + 16 * ROWB, of, db);
+                    quarter(db);
+                    fence();
+                }
+    #pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    dvacc[db] = mfma32<BF16>(ug[db], pp[1], dvacc[db]);
+                    dkacc[db] = mfma32<BF16>(uq[db], ss[1], dkacc[db]);
+                    quarter(ND + db);
+                    fence();
+                }
+            };
+            // the element-wise work of rows 32..63, a quarter beside every four products
+            // of rows 0..31
+            // (its LSE and D values are read before the transposed operands: LDS reads
+            // complete in order, so a later read would wait for all of those)
+            f32x4 l1[4], dd1[4];
+            accum(0, pb, sb, [&] {
+    #pragma unroll
+                for (int qtr = 0; qtr < 4; ++qtr) {
+                    const int o = 32 + 8 * h + 16 * (qtr >> 1) + 4 * (qtr & 1);
+                    l1[qtr] = *(const f32x4*)(Ls + o);
+                    dd1[qtr] = *(const f32x4*)(Ds + o);
+                }
+            }, [&](int qtr) {
+                const int p = qtr >> 1, e0 = 4 * (qtr & 1);
+                dkdv_probs4<BF16, MASK>(s1, d1, l1[qtr], dd1[qtr], a.c, lim - 32, p, e0, pb1[p], sb1[p]);
+            });
+            accum(1, pb1, sb1, [] {}, [](int) {});
         };
 
-        // query tiles upward from the diagonal (the first ones may hold rows that do
-        // not yet see some keys of the block), for each query head of the group in
-        // turn: step it covers head it / n_tiles, tile t0 + it % n_tiles
+        // Query tiles upward from the diagonal, for each query head of the group in
+        // turn.  Causal: the first n_mt tiles of a head hold rows that do not yet see
+        // every key of the block and run the masked body (a wave whose keys no row of
+        // the tile sees skips it); all later tiles run the unmasked body.  Separate
+        // loops keep one body per loop, so the accumulators never meet at a branch join.
+        int n_mt = 0;
+        if (CAUSAL && n_tiles > 0) {
+            const int last_partial = k0 + CK - 2 - off;   // last row that misses a key of the block
+            n_mt = last_partial < 0 ? 0 : min(n_tiles, last_partial / CQ - t0 + 1);
+        }
         const int n_steps = n_tiles * a.group;
         if (n_steps > 0) load_tile(0, t0, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // two tiles per trip, so that each step reads one fixed LDS stage
-        int g_next = 0, t_next = 0;   // head and tile offset of step it + 1
-        auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
-            const int tile = t0 + t_next;
-            if (++t_next == n_tiles) {
-                t_next = 0;
-                ++g_next;
-            }
-            if (it + 1 < n_steps) load_tile(g_next, t0 + t_next, nxt);
-            const int i0 = tile * CQ;
-            // causal: a wave whose keys every row of the tile sees needs no mask, and
-            // one whose keys no row sees yet skips the tile
-            if (!CAUSAL || kw + 31 <= i0 + off) step(cur, i0, std::false_type{});
-            else if (kw <= i0 + CQ - 1 + off) step(cur, i0, std::true_type{});
+        int it = 0;                    // steps done (the stage of step it is it & 1)
+        // load the tile after (g, tile): the head's next tile, else the next head's first
+        auto prefetch = [&](int g, int tile, unsigned char* nxt) {
+            if (tile + 1 < t0 + n_tiles) load_tile(g, tile + 1, nxt);
+            else if (g + 1 < a.group) load_tile(g + 1, t0, nxt);
+        };
+        auto clean_one = [&](int g, int& tile, unsigned char* cur, unsigned char* nxt) {
+            prefetch(g, tile, nxt);
+            step(cur, tile * CQ, std::false_type{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            ++tile;
+            ++it;
         };
     #pragma clang loop unroll(disable)
-        for (int it = 0; it < n_steps; it += 2) {
-            one(it, stage0, stage1);
-            if (it + 1 < n_steps) one(it + 1, stage1, stage0);
+        for (int g = 0; g < a.group && n_tiles > 0; ++g) {
+            int tile = t0;
+    #pragma clang loop unroll(disable)
+            for (; tile < t0 + n_mt; ++tile, ++it) {
+                unsigned char* cur = (it & 1) ? stage1 : stage0;
+                unsigned char* nxt = (it & 1) ? stage0 : stage1;
+                prefetch(g, tile, nxt);
+                const int i0 = tile * CQ;
+                if (kw <= i0 + CQ - 1 + off) step(cur, i0, std::true_type{});
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
+            if ((it & 1) && tile < t0 + n_tiles) clean_one(g, tile, stage1, stage0);
+    #pragma clang loop unroll(disable)
+            while (tile < t0 + n_tiles) {
+                clean_one(g, tile, stage0, stage1);
+                if (tile < t0 + n_tiles) clean_one(g, tile, stage1, stage0);
+            }
         }
 
         if (kok) {
