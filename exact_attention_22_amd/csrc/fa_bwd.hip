@@ -265,6 +265,36 @@ __device__ __forceinline__ void scores(const unsigned char* T1, const unsigned c
     }
 }
 
+// Store a wave's 32 x D output tile held in the transposed-accumulator layout
+// (acc[db] register 4g + i is column 32 db + 8g + 4h + i of row l32) as 16-bit
+// values times `mul`: the tile goes through the wave's own LDS region `reg`
+// (32 rows, 16-byte chunks XOR-swizzled by row) and leaves one 16-byte chunk per
+// lane, so each store instruction covers whole rows.  Rows r with row0 + r >= n
+// are not stored.  The caller guarantees no other wave uses `reg` meanwhile.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float mul, unsigned char* reg,
+                                                  uint16_t* dst, int row_stride, int row0, int n, int lane) {
+    constexpr int ROWB = D * 2, CH = ROWB / 16, RPI = 1024 / ROWB;
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x2 v2 = {pack2<BF16>(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                              pack2<BF16>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+            const int c = 4 * db + g;
+            *(u32x2*)(reg + l32 * ROWB + ((c ^ (l32 & (CH - 1))) << 4) + 8 * h) = v2;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane % CH;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+        const int r = it * RPI + lane / CH;
+        const u32x4 v4 = *(const u32x4*)(reg + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+        if (row0 + r < n) *(u32x4*)(dst + (size_t)(row0 + r) * row_stride + 8 * c) = v4;
+    }
+}
+
 // ---- dQ ---------------------------------------------------------------------
 // dS^T for one 32-key block (register 8p + e stands for key k0 + 32kb + 16p + 8h
 // + e), packed as the B operand of dQ^T += K^T dS^T.  MASK zeroes P from key
@@ -375,40 +405,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // two tiles per trip, so that each step reads one fixed LDS stage
-        auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
+        // the masked tiles (per-wave visibility, stage chosen at run time), then the
+        // clean ones two per trip so that each step reads one fixed LDS stage: one
+        // body per loop, so the accumulators never meet at a branch join
+        int it = 0;
+    #pragma clang loop unroll(disable)
+        for (; it < n_masked; ++it) {
             const int tile = n_tiles - 1 - it;
+            unsigned char* cur = (it & 1) ? stage1 : stage0;
+            unsigned char* nxt = (it & 1) ? stage0 : stage1;
             if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
             const int k0 = tile * BK;
-            if (it < n_masked) {
-                if (qw < Nq && (!CAUSAL || k0 <= min(qw + 31, Nq - 1) + off)) {
-                    int bound = Nk - k0;
-                    if (CAUSAL) bound = min(bound, qi + off - k0 + 1);
-                    step(cur, cur + TILE, bound - 8 * h, std::true_type{});
-                }
-            } else {
-                step(cur, cur + TILE, BK, std::false_type{});
+            if (qw < Nq && (!CAUSAL || k0 <= min(qw + 31, Nq - 1) + off)) {
+                int bound = Nk - k0;
+                if (CAUSAL) bound = min(bound, qi + off - k0 + 1);
+                step(cur, cur + TILE, bound - 8 * h, std::true_type{});
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+        }
+        auto clean_one = [&](unsigned char* cur, unsigned char* nxt) {
+            const int tile = n_tiles - 1 - it;
+            if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+            step(cur, cur + TILE, BK, std::false_type{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            ++it;
         };
+        if ((it & 1) && it < n_tiles) clean_one(stage1, stage0);
     #pragma clang loop unroll(disable)
-        for (int it = 0; it < n_tiles; it += 2) {
-            one(it, stage0, stage1);
-            if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
+        while (it < n_tiles) {
+            clean_one(stage0, stage1);
+            if (it < n_tiles) clean_one(stage1, stage0);
         }
 
-        if (qok) {
-            uint16_t* dst = a.dq + sg.q + (size_t)qi * sg.sq;
-    #pragma unroll
-            for (int db = 0; db < ND; ++db)
-    #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
-                    const u32x2 v2 = {pack2<BF16>(x[0] * a.scale, x[1] * a.scale), pack2<BF16>(x[2] * a.scale, x[3] * a.scale)};
-                    *(u32x2*)(dst + 32 * db + 8 * g + 4 * h) = v2;
-                }
-        }
+        // the walk ended with a barrier, so the stages are free: each wave stages
+        // its 32 rows in its own quarter of stage 0
+        store_rows_staged<BF16, D>(dqacc, a.scale, stage0 + w * (32 * ROWB), a.dq + sg.q, sg.sq, qw, Nq, lane);
     };
     for_items<CAUSAL, !VARLEN>(a.n_qtiles, a.BH, run_item);
 }
@@ -668,22 +701,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             }
         }
 
-        if (kok) {
-            uint16_t* dkp = a.dk + sg.k + (size_t)kj * sg.sk;
-            uint16_t* dvp = a.dv + sg.k + (size_t)kj * sg.sk;
-    #pragma unroll
-            for (int db = 0; db < ND; ++db)
-    #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int c0 = 32 * db + 8 * g + 4 * h;
-                    const u32x2 k2 = {pack2<BF16>(dkacc[db][4 * g] * a.scale, dkacc[db][4 * g + 1] * a.scale),
-                                      pack2<BF16>(dkacc[db][4 * g + 2] * a.scale, dkacc[db][4 * g + 3] * a.scale)};
-                    const u32x2 v2 = {pack2<BF16>(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
-                                      pack2<BF16>(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
-                    *(u32x2*)(dkp + c0) = k2;
-                    *(u32x2*)(dvp + c0) = v2;
-                }
-        }
+        // the walk ended with a barrier, so the stages are free: each wave stages its
+        // 32 dK rows in its quarter of stage 0 and its dV rows in stage 1
+        store_rows_staged<BF16, D>(dkacc, a.scale, stage0 + w * (32 * ROWB), a.dk + sg.k, sg.sk, kw, Nk, lane);
+        store_rows_staged<BF16, D>(dvacc, 1.f, stage1 + w * (32 * ROWB), a.dv + sg.k, sg.sk, kw, Nk, lane);
     };
     for_items<CAUSAL, !VARLEN>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
 }
