@@ -18,6 +18,10 @@ Workloads (Q, K, V iid N(0, 1), layout [B, H, N, d], scale = 1/sqrt(d)):
   decode_paged    as decode_gqa with K/V in a paged cache of 16-row pages
                   [num_pages, 16, H_kv, d], pages assigned by a seeded
                   permutation (a fragmented cache); q [B, H, d]
+  decode_varlen   one query row per sequence over 16 packed sequences of keys,
+                  lengths log-uniform in [512, 32768] (seeded), H=32 query heads
+                  on H_kv=8 K/V heads, d=128 fp16, 16 splits per sequence;
+                  q [B, H, d], K, V [total_k, H_kv, d]
 These follow the shapes the pages benchmark (randn fp16, d in {64, 128},
 N from 1K to 16K) -- no dataset is involved.
 """
@@ -44,7 +48,8 @@ class Workload:
     splits: int = 0          # > 0: decode through split-KV + combine
     seed: int = 42
     H_kv: int = 0            # K/V heads when grouped (0: H)
-    seqlens: tuple = ()      # non-empty: packed layout with these lengths (queries = keys)
+    seqlens: tuple = ()      # non-empty: packed layout with these lengths (queries = keys; with
+                             # splits > 0, one query row per sequence and these key lengths)
     page_size: int = 0       # > 0: decode from a paged K/V cache with pages of this many rows
 
     @property
@@ -63,6 +68,7 @@ def log_uniform_lengths(n, lo, hi, seed):
 
 
 _VARLEN_LENS = log_uniform_lengths(16, 64, 8192, 47)
+_DECODE_VARLEN_LENS = log_uniform_lengths(16, 512, 32768, 51)
 
 WORKLOADS = [
     Workload("tiny", 1, 1, 128, 128, 64, F16, False, seed=42),
@@ -74,6 +80,8 @@ WORKLOADS = [
     Workload("decode_paged", 8, 32, 1, 32768, 128, F16, False, splits=16, seed=49, H_kv=8, page_size=16),
     Workload("varlen_gqa", len(_VARLEN_LENS), 32, max(_VARLEN_LENS), max(_VARLEN_LENS), 128, BF16, True,
              seed=47, H_kv=8, seqlens=_VARLEN_LENS),
+    Workload("decode_varlen", len(_DECODE_VARLEN_LENS), 32, 1, max(_DECODE_VARLEN_LENS), 128, F16, False,
+             splits=16, seed=50, H_kv=8, seqlens=_DECODE_VARLEN_LENS),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -121,6 +129,36 @@ def make_varlen(w: Workload, device="cpu"):
         del x
     cu = cu_seqlens(w.seqlens).to(device)
     return (*out, cu, cu.clone())
+
+
+def make_varlen_decode(w: Workload, device="cpu", seqlens=None, spare_rows=0, fill=float("nan")):
+    """One query row per sequence over packed keys.
+
+    Returns q [B, H, d]; k, v [total_k, H_kv, d] with sequence b in rows
+    [cu[b], cu[b+1]) (lengths w.seqlens unless given) followed by `spare_rows`
+    rows of `fill` (NaN by default: a kernel that reads past the last sequence
+    produces NaN); cu_seqlens_k int32 [B + 1].  Q, then the keys, then the values
+    are drawn as in make_qkv.
+    """
+    lens = [int(n) for n in (seqlens if seqlens is not None else w.seqlens)]
+    B, hk, total = len(lens), w.H_kv or w.H, sum(lens)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    out = []
+    for shape in ((B, w.H, w.d), (total, hk, w.d), (total, hk, w.d)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+        if w.mult != 1.0:
+            x.mul_(w.mult)
+        out.append(x.to(w.dtype))
+        del x
+    q, k_tok, v_tok = out
+    kv = []
+    for tok in (k_tok, v_tok):
+        if spare_rows:
+            pad = torch.full((spare_rows, hk, w.d), fill, dtype=w.dtype, device=device)
+            tok = torch.cat([tok, pad])
+        kv.append(tok)
+    return q, kv[0], kv[1], cu_seqlens(lens).to(device)
 
 
 def make_partials(S, B, H, Nq, d, seed=7, device="cpu", empty_every=0):

@@ -319,6 +319,33 @@ class Oracle:
             lse_part[:, b] = lb[:, 0]
         return o_part, lse_part
 
+    def split_partials_varlen(self, q, k, v, cu_seqlens_k, scale, num_splits, nthreads=None):
+        """Per-split normalised partials of one query row per packed sequence (the
+        varlen interface, Ringi, "Lecture 25", section 7, with split-KV for decode,
+        LLM Infra Atlas, "FA2: parallelism", section 2): q [B, H, d]; sequence b's
+        keys are rows [cu[b], cu[b+1]) of k, v [total_k, H_kv, d], cut into
+        num_splits chunks of ceil(len_b / num_splits) keys (split_ranges applied
+        per sequence, as for the paged cache).  Returns o_part [S, B, H, 1, d] and
+        lse_part [S, B, H, 1]."""
+        B, H, d = q.shape
+        S = num_splits
+        cu = [int(x) for x in cu_seqlens_k]
+        if len(cu) != B + 1:
+            raise ValueError("cu_seqlens_k must hold B + 1 offsets")
+        o_part = np.zeros((S, B, H, 1, d))
+        lse_part = np.full((S, B, H, 1), -np.inf)
+        for b in range(B):
+            lo, hi = cu[b], cu[b + 1]
+            if hi == lo:
+                continue
+            kb = k[lo:hi].permute(1, 0, 2).unsqueeze(0).contiguous()
+            vb = v[lo:hi].permute(1, 0, 2).unsqueeze(0).contiguous()
+            ob, lb = self.split_partials(q[b:b + 1, :, None, :].contiguous(), kb, vb, False, scale, S,
+                                         nthreads=nthreads)
+            o_part[:, b] = ob[:, 0]
+            lse_part[:, b] = lb[:, 0]
+        return o_part, lse_part
+
     # -- split-KV ---------------------------------------------------------
     @staticmethod
     def split_ranges(Nk, num_splits):

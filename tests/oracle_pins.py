@@ -666,6 +666,68 @@ def pin_paged_splits(orc):
     _close(lc.reshape(H), lse[0], 1e-12, "paged combined LSE")
 
 
+# -- packed split-KV decode (Ringi, "Lecture 25", section 7; LLM Infra Atlas, section 2) --
+def pin_varlen_decode_splits(orc):
+    """Packed-sequence partials split each sequence into chunks of ceil(len / S)
+    keys (10 keys, S = 4: [0,3) [3,6) [6,9) [9,10); 2 keys: [0,1) [1,2) and two
+    empty splits); every chunk equals attention over that key range of the
+    sequence alone, and the merged partials equal varlen attention with one query
+    row per sequence."""
+    H, H_kv, d, S = 4, 2, 8, 4
+    lens = [10, 0, 2]
+    B, total = len(lens), sum(lens)
+    for dt in DTYPES:
+        q = _rand((B, H, d), dt, 541)
+        k = _rand((total, H_kv, d), dt, 542)
+        v = _rand((total, H_kv, d), dt, 543)
+        cu = [0, 10, 10, 12]
+        op, lp = orc.split_partials_varlen(q, k, v, cu, 0.35, S, nthreads=1)
+        ranges = {0: [(0, 3), (3, 6), (6, 9), (9, 10)], 2: [(0, 1), (1, 2), (2, 2), (2, 2)]}
+        for b, rs in ranges.items():
+            kb = k[cu[b]:cu[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+            vb = v[cu[b]:cu[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+            for s_, kr in enumerate(rs):
+                if kr[0] == kr[1]:
+                    assert np.all(op[s_, b] == 0) and np.all(np.isneginf(lp[s_, b])), "empty split"
+                    continue
+                ro, rl = orc.attention_gqa(q[b:b + 1, :, None, :].contiguous(), kb, vb, False, 0.35,
+                                           key_range=kr, nthreads=1)
+                _close(op[s_, b], ro[0], 1e-12, f"varlen split {s_} O, sequence {b}, {dt}")
+                _close(lp[s_, b], rl[0], 1e-12, f"varlen split {s_} LSE, sequence {b}, {dt}")
+        assert np.all(op[:, 1] == 0) and np.all(np.isneginf(lp[:, 1])), "empty sequence gives empty splits"
+        oc, lc = orc.combine(op, lp)
+        ro, rl = orc.attention_varlen(q, k, v, list(range(B + 1)), cu, False, 0.35, nthreads=1)
+        _close(oc.reshape(B, H, d), ro, 1e-12, f"varlen combined O, {dt}")
+        _close(lc.reshape(B, H), rl.T, 1e-12, f"varlen combined LSE, {dt}")
+
+
+def pin_varlen_decode_matches_paged(orc):
+    """The same keys as packed sequences and as a shuffled paged cache (pages of
+    3 rows) give the same partials: two independent ways of locating a
+    sequence's keys."""
+    H, H_kv, d, S, ps = 2, 1, 16, 3, 3
+    lens = [7, 1, 5]
+    B, N = len(lens), max(lens)
+    q = _rand((B, H, d), torch.float16, 551)
+    kd = _rand((B, H_kv, N, d), torch.float16, 552)
+    vd = _rand((B, H_kv, N, d), torch.float16, 553)
+    # packed rows of each sequence, back to back
+    k = torch.cat([kd[b, :, :n].permute(1, 0, 2) for b, n in enumerate(lens)]).contiguous()
+    v = torch.cat([vd[b, :, :n].permute(1, 0, 2) for b, n in enumerate(lens)]).contiguous()
+    cu = [0, 7, 8, 13]
+    P = sum(-(-n // ps) for n in lens)
+    order = list(np.random.default_rng(554).permutation(P))
+    kc, table = _paged_from_contiguous(kd, lens, ps, order)
+    vc, _ = _paged_from_contiguous(vd, lens, ps, order)
+    op, lp = orc.split_partials_varlen(q, k, v, cu, 0.25, S, nthreads=1)
+    pp, pl = orc.split_partials_paged(q, kc, vc, table, lens, 0.25, S, nthreads=1)
+    _close(op, pp, 0.0, "packed vs paged partial O")
+    _close(lp, pl, 0.0, "packed vs paged partial LSE")
+
+
+VARLEN_DECODE_PINS = [pin_varlen_decode_splits, pin_varlen_decode_matches_paged]
+
+
 # -- FP8 (e4m3) inputs with per-block scales (Ringi, "Lecture 25", section 5.4) --
 def pin_e4m3_decode(orc=None):
     """Values the e4m3 format definition fixes (OCP 8-bit floating point, E4M3FN:

@@ -121,6 +121,43 @@ def test_paged_gather_mutants_are_caught(kind):
     assert caught, f"no paged pin catches the {kind} mutant"
 
 
+@pytest.mark.parametrize("kind", ["first_sequence", "offset_of_next", "one_split"])
+def test_varlen_decode_mutants_are_caught(kind):
+    """Plausible mistakes in locating a packed sequence's keys, or in its split
+    rule, fail the packed-decode pins."""
+    class Broken(oracle.Oracle):
+        def split_partials_varlen(self, q, k, v, cu_seqlens_k, scale, num_splits, nthreads=None):
+            B, H, d = q.shape
+            cu = [int(x) for x in cu_seqlens_k]
+            o_part = np.zeros((num_splits, B, H, 1, d))
+            lse_part = np.full((num_splits, B, H, 1), -np.inf)
+            for b in range(B):
+                lo, hi = cu[b], cu[b + 1]
+                if kind == "first_sequence":
+                    lo, hi = cu[0], cu[1]
+                elif kind == "offset_of_next":
+                    lo, hi = min(lo + 1, cu[-1] - 1), min(hi + 1, cu[-1])
+                if hi <= lo:
+                    continue
+                kb = k[lo:hi].permute(1, 0, 2).unsqueeze(0).contiguous()
+                vb = v[lo:hi].permute(1, 0, 2).unsqueeze(0).contiguous()
+                S = 1 if kind == "one_split" else num_splits
+                ob, lb = self.split_partials(q[b:b + 1, :, None, :].contiguous(), kb, vb, False, scale, S,
+                                             nthreads=nthreads)
+                o_part[:S, b] = ob[:, 0]
+                lse_part[:S, b] = lb[:, 0]
+            return o_part, lse_part
+
+    orc = Broken()
+    caught = 0
+    for pin in oracle_pins.VARLEN_DECODE_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, IndexError, RuntimeError):
+            caught += 1
+    assert caught, f"no packed-decode pin catches the {kind} mutant"
+
+
 FP8_MUTANTS = {
     # decoder: exponent bias 8 instead of 7
     "decode_bias": ("normal = sign * np.ldexp(1.0 + mant / 8.0, expo - 7)",

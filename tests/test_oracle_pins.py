@@ -5,7 +5,7 @@ import pytest
 from tests import oracle_pins
 
 
-@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + oracle_pins.FP8_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + oracle_pins.FP8_PINS + oracle_pins.VARLEN_DECODE_PINS, ids=lambda p: p.__name__)
 def test_pin(oracle_lib, pin):
     pin(oracle_lib)
 
