@@ -9,7 +9,9 @@ One step = one pass of the whole path over resident synthetic inputs:
     (B=8, H=32, Nq=1, Nk=32768, d=128, fp16, 16 splits), the same with the 32
     query heads sharing 8 K/V heads (decode_gqa), and the same again with K/V in
     a paged cache of 16-row pages scattered by a seeded permutation
-    (decode_paged), and
+    (decode_paged), and one query row per sequence over 16 packed sequences of
+    keys (decode_varlen: lengths log-uniform in [512, 32768], 129054 keys, the
+    32 query heads on 8 K/V heads, 16 splits per sequence), and
   * bwd: fa_bwd on the long-context causal workload (dO ~ N(0,1)), and
   * fp8: fa_fwd_fp8 on the long-context workload's inputs quantized to e4m3
     per block (quantized once, untimed), and
@@ -43,7 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_attention_22_amd import fa                          # noqa: E402
-from exact_attention_22_amd.inputs import BY_NAME, make_paged, make_qkv, make_varlen     # noqa: E402
+from exact_attention_22_amd.inputs import BY_NAME, make_paged, make_qkv, make_varlen, make_varlen_decode  # noqa: E402
 
 METRIC = "attn fwd TFLOPS & % MFMA peak (fp16 d=128 causal N=8K); decode HBM GB/s"
 PEAK_TFLOPS = 2500.0         # MI355X dense bf16/fp16 MFMA
@@ -163,7 +165,8 @@ def stats_us(times_ms):
             "min_us": 1e3 * min(times_ms)}
 
 
-LEGS = ["prefill", "prefill_d64", "causal_d128", "decode", "decode_gqa", "decode_paged", "varlen", "bwd", "fp8"]
+LEGS = ["prefill", "prefill_d64", "causal_d128", "decode", "decode_gqa", "decode_paged", "decode_varlen", "varlen",
+        "bwd", "fp8"]
 
 
 def main():
@@ -190,6 +193,7 @@ def main():
 
     wp, wd, wv, wg = BY_NAME["long_causal"], BY_NAME["decode"], BY_NAME["varlen_gqa"], BY_NAME["decode_gqa"]
     wpg, w64, w128 = BY_NAME["decode_paged"], BY_NAME["prefill_d64"], BY_NAME["causal_d128"]
+    wdv = BY_NAME["decode_varlen"]
     stream = torch.cuda.current_stream()
     calls = {}    # leg -> list of (sub-leg name, callable); each sub-leg is timed by its own events
 
@@ -236,6 +240,16 @@ def main():
                                                o_part=pop, lse_part=plp, stream=stream)
         comb_p = lambda: fa.splitkv_combine(pop, plp, wpg.dtype, out=po, lse=plse, stream=stream)  # noqa: E731
         calls["decode_paged"] = [("split", split_p), ("combine", comb_p), ("total", lambda: (split_p(), comb_p()))]
+    if on["decode_varlen"]:
+        vdq, vdk, vdv, vdcu = make_varlen_decode(wdv, device=dev)
+        vdop = torch.empty((wdv.splits, wdv.B, wdv.H, 1, wdv.d), dtype=torch.float32, device=dev)
+        vdlp = torch.empty((wdv.splits, wdv.B, wdv.H, 1), dtype=torch.float32, device=dev)
+        vdo = torch.empty((wdv.B, wdv.H, 1, wdv.d), dtype=wdv.dtype, device=dev)
+        vdlse = torch.empty((wdv.B, wdv.H, 1), dtype=torch.float32, device=dev)
+        split_v = lambda: fa.fwd_splitkv_varlen(vdq, vdk, vdv, vdcu, max(wdv.seqlens), wdv.splits,  # noqa: E731
+                                                scale=wdv.scale, o_part=vdop, lse_part=vdlp, stream=stream)
+        comb_v = lambda: fa.splitkv_combine(vdop, vdlp, wdv.dtype, out=vdo, lse=vdlse, stream=stream)  # noqa: E731
+        calls["decode_varlen"] = [("split", split_v), ("combine", comb_v), ("total", lambda: (split_v(), comb_v()))]
     if on["varlen"]:
         vq, vk, vv, vcq, vck = make_varlen(wv, device=dev)
         vo = torch.empty_like(vq)
@@ -405,6 +419,20 @@ def main():
         if args.only == "decode_paged":
             out.update({"value": out["decode_paged"]["GB_per_s"], "unit": "GB/s", "dtype": "f16"})
             cfg["workload"] = "decode_paged: B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 fp16 16 splits, 16-row pages"
+    if on["decode_varlen"]:
+        # bytes the method must move: Q, O (B*H*d each), every sequence's K and V
+        # once (total_k*H_kv*d each), LSE, and the B+1 offsets
+        tk = sum(wdv.seqlens)
+        vgb = 2 * 2 * wdv.B * wdv.H * wdv.d + 2 * 2 * tk * wdv.H_kv * wdv.d + 4 * wdv.B * wdv.H + 4 * (wdv.B + 1)
+        out["decode_varlen"], out["roofline_decode_varlen"] = decode_block(
+            "decode_varlen", vgb, vgb - 2 * wdv.B * wdv.H * wdv.d - 4 * wdv.B * wdv.H,
+            "decode_kernel<fp16, d=128, 4 query heads per workgroup, packed>", "decode_varlen")
+        cfg["decode_varlen"] = {"sequences": wdv.B, "keys": tk, "max_seqlen_k": max(wdv.seqlens), "H": wdv.H,
+                                "H_kv": wdv.H_kv, "Nq": 1, "d": wdv.d, "dtype": "fp16", "splits": wdv.splits}
+        if args.only == "decode_varlen":
+            out.update({"value": out["decode_varlen"]["GB_per_s"], "unit": "GB/s", "dtype": "f16"})
+            cfg["workload"] = ("decode_varlen: 16 packed sequences, 129054 keys, H=32 H_kv=8 Nq=1 d=128 fp16, "
+                               "16 splits per sequence")
     if on["varlen"]:
         fl = sum(attn_flops(1, wv.H, n, n, wv.d, wv.causal) for n in wv.seqlens)
         t_var = leg_ms("varlen", mean)

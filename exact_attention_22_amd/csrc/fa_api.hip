@@ -298,6 +298,26 @@ fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v
     return from_hip(fa::launch_decode(p, (hipStream_t)stream));
 }
 
+fa_status fa_fwd_splitkv_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens_k,
+                                float* o_part, float* lse_part,
+                                int B, int H, int H_kv, int total_k, int max_seqlen_k, int d,
+                                float scale, int num_splits, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !cu_seqlens_k || !o_part || !lse_part) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || num_splits < 1) return FA_ERR_SHAPE;
+    if (total_k < 1 || max_seqlen_k < 1 || max_seqlen_k > total_k) return FA_ERR_SHAPE;
+    if (count4(total_k, H_kv, d, 1) < 0 || count4(B, H, d, num_splits) < 0) return FA_ERR_SHAPE;
+    if ((int64_t)B * H > INT32_MAX || B == INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) || ((uintptr_t)lse_part & 3u) ||
+        ((uintptr_t)cu_seqlens_k & 3u))
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdParams p{q, k, v, o_part, lse_part, B, H, 1, max_seqlen_k, d, false, dtype == FA_BF16, scale,
+                    num_splits, true, nullptr, cu_seqlens_k, H_kv, B, total_k};
+    return from_hip(fa::launch_decode(p, (hipStream_t)stream));
+}
+
 fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                      const float* k_descale, const float* v_descale, void* o, float* lse,
                      int B, int H, int H_kv, int Nq, int Nk, int d, int causal, float scale, void* stream) {

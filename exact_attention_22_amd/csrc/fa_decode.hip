@@ -32,6 +32,13 @@
 // own key's page, and the page entries of the next step are fetched one step
 // ahead so the indirection adds no latency.  Each sequence has its own length
 // and is split into num_splits equal chunks.
+//
+// Packed sequences (the varlen interface with cumulative offsets instead of
+// padding, Ringi, "Lecture 25", section 7; split-KV for decode, LLM Infra Atlas,
+// section 2): sequence b's keys are rows [cu_k[b], cu_k[b+1]) of k, v [total_k,
+// H_kv, d], so a key row of one head is again 256 contiguous bytes (d = 128),
+// H_kv * d elements after the previous one; each sequence is split into
+// num_splits chunks of its own length, as in the paged mode.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -53,7 +60,13 @@ struct DecArgs {
     const int* seqlens;       // [B]
     int page_shift;           // log2(page_size)
     int max_pages, num_pages;
+    // packed sequences: key offsets [B + 1], total rows of k and v, longest sequence
+    const int* cu_k;
+    int total_k, max_k;
 };
+
+// Where the keys of a decode come from.
+enum KvLayout { KV_DENSE = 0, KV_PAGED = 1, KV_PACKED = 2 };
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -92,10 +105,11 @@ __device__ __forceinline__ float dot2(u32 a, u32 b, float acc) {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
 }
 
-// GP: query heads per workgroup (a divisor of the group size).  PAGED: k and v
-// are the paged caches.
-template <bool BF16, int D, int GP, bool PAGED>
+// GP: query heads per workgroup (a divisor of the group size).  KV: dense
+// [B, H_kv, Nk, d] keys, the paged caches, or packed sequences.
+template <bool BF16, int D, int GP, int KV>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
+    constexpr bool PAGED = KV == KV_PAGED;
     constexpr int CH = D / 8;          // lanes per key row
     constexpr int KPI = 64 / CH;       // key rows per wavefront load
     constexpr int U = GP >= 4 ? 4 : 8; // key groups in flight per step
@@ -126,6 +140,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         kg = a.k;
         vg = a.v;
         bt = a.block_table + (size_t)b * a.max_pages;
+    } else if constexpr (KV == KV_PACKED) {
+        const int b = bh0 / a.H;
+        hk = (bh0 % a.H) / a.group;
+        // offsets outside [0, total_k], decreasing or longer than the declared
+        // maximum leave the sequence's rows unwritten
+        const int k_lo = a.cu_k[b], k_hi = a.cu_k[b + 1];
+        if (k_lo < 0 || k_hi < k_lo || k_hi > a.total_k || k_hi - k_lo > a.max_k) return;
+        const int len = k_hi - k_lo;
+        const int chunk = (len + a.S - 1) / a.S;
+        ks = min(len, split * chunk);
+        ke = min(len, ks + chunk);
+        kg = a.k + ((size_t)k_lo * a.H_kv + hk) * D;
+        vg = a.v + ((size_t)k_lo * a.H_kv + hk) * D;
     } else {
         ks = min(a.Nk, split * a.split_chunk);
         ke = min(a.Nk, ks + a.split_chunk);
@@ -173,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
                 row = (((size_t)pg << a.page_shift) + (key[u] & ((1 << a.page_shift) - 1))) * a.H_kv + hk;
             } else {
                 ok[u] = key[u] < ke;
-                row = (size_t)key[u];
+                row = KV == KV_PACKED ? (size_t)key[u] * a.H_kv : (size_t)key[u];
             }
             if (ok[u]) {
                 kr[u] = *(const u32x4*)(kg + row * D + 8 * c);
@@ -326,22 +353,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (lane == 0) lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
-template <bool BF16, int D, bool PAGED>
+template <bool BF16, int D, int KV>
 hipError_t launch_dec(const DecArgs& a, int gp, int blocks, hipStream_t stream) {
     switch (gp) {
-        case 8: hipLaunchKernelGGL((decode_kernel<BF16, D, 8, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<BF16, D, 1, PAGED>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_kernel<BF16, D, 8, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
     }
     return hipGetLastError();
 }
 
-template <bool PAGED>
+template <int KV>
 hipError_t launch_dec_d(const DecArgs& a, int d, bool bf16, int gp, int blocks, hipStream_t stream) {
-    if (d == 128) return bf16 ? launch_dec<true, 128, PAGED>(a, gp, blocks, stream)
-                              : launch_dec<false, 128, PAGED>(a, gp, blocks, stream);
-    return bf16 ? launch_dec<true, 64, PAGED>(a, gp, blocks, stream) : launch_dec<false, 64, PAGED>(a, gp, blocks, stream);
+    if (d == 128) return bf16 ? launch_dec<true, 128, KV>(a, gp, blocks, stream)
+                              : launch_dec<false, 128, KV>(a, gp, blocks, stream);
+    return bf16 ? launch_dec<true, 64, KV>(a, gp, blocks, stream) : launch_dec<false, 64, KV>(a, gp, blocks, stream);
 }
 
 }  // namespace
@@ -371,8 +398,12 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
     a.num_pages = p.num_pages;
     a.page_shift = 0;
     while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
-    if (p.block_table) return launch_dec_d<true>(a, p.d, p.bf16, gp, (int)blocks, stream);
-    return launch_dec_d<false>(a, p.d, p.bf16, gp, (int)blocks, stream);
+    a.cu_k = p.cu_k;
+    a.total_k = p.total_k;
+    a.max_k = p.Nk;
+    if (p.block_table) return launch_dec_d<KV_PAGED>(a, p.d, p.bf16, gp, (int)blocks, stream);
+    if (p.varlen) return launch_dec_d<KV_PACKED>(a, p.d, p.bf16, gp, (int)blocks, stream);
+    return launch_dec_d<KV_DENSE>(a, p.d, p.bf16, gp, (int)blocks, stream);
 }
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,

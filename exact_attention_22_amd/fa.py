@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 SYMBOLS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv",
-           "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_paged", "fa_fwd_splitkv_varlen", "fa_splitkv_combine", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_bwd_gqa", "fa_bwd_gqa_noalloc", "fa_bwd_varlen", "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_str")
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
@@ -51,6 +51,8 @@ def lib():
         L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         L.fa_fwd_splitkv_paged.restype = i
         L.fa_fwd_splitkv_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+        L.fa_fwd_splitkv_varlen.restype = i
+        L.fa_fwd_splitkv_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         L.fa_splitkv_combine.restype = i
         L.fa_splitkv_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -270,6 +272,50 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits=16, sca
     """fwd_splitkv_paged followed by the combine: O [B, H, 1, d], LSE [B, H, 1]."""
     o_part, lse_part = fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits, scale,
                                          o_part, lse_part, stream)
+    return splitkv_combine(o_part, lse_part, q.dtype, stream=stream)
+
+
+def fwd_splitkv_varlen(q, k, v, cu_seqlens_k, max_seqlen_k, num_splits, scale=None, o_part=None, lse_part=None,
+                       stream=None):
+    """Split-KV partials of one query row per packed sequence.
+
+    q [B, H, d]; k, v [total_k, H_kv, d] with sequence b in rows
+    [cu_seqlens_k[b], cu_seqlens_k[b+1]) (int32 [B + 1] on the device).  Returns
+    o_part [S, B, H, 1, d] and lse_part [S, B, H, 1] (fp32) for splitkv_combine.
+    """
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [B, H, d] and k, v [total_k, H_kv, d]")
+    B, H, d = q.shape
+    total_k, H_kv = k.shape[:2]
+    if tuple(k.shape) != (total_k, H_kv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [total_k, H_kv, d] with q's d")
+    if tuple(cu_seqlens_k.shape) != (B + 1,):
+        raise ValueError("cu_seqlens_k must be [B + 1]")
+    qp, kp, vp = (_dev_tensor(t, n, q.dtype) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    cup = _dev_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    S = int(num_splits)
+    # a sequence whose offsets break the contract leaves its partials unwritten;
+    # partials allocated here start as empty splits (O = 0, LSE = -inf)
+    if o_part is None:
+        o_part = torch.zeros((S, B, H, 1, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.full((S, B, H, 1), -math.inf, dtype=torch.float32, device=q.device)
+    if tuple(o_part.shape) != (S, B, H, 1, d) or tuple(lse_part.shape) != (S, B, H, 1):
+        raise ValueError("o_part must be [S, B, H, 1, d] and lse_part [S, B, H, 1]")
+    opp = _dev_tensor(o_part, "o_part", torch.float32)
+    lpp = _dev_tensor(lse_part, "lse_part", torch.float32)
+    _check(lib().fa_fwd_splitkv_varlen(qp, kp, vp, cup, opp, lpp, B, H, H_kv, total_k, int(max_seqlen_k), d,
+                                       _scale(scale, d), S, _DTYPES[q.dtype], _stream(stream)))
+    return o_part, lse_part
+
+
+def decode_varlen(q, k, v, cu_seqlens_k, max_seqlen_k, num_splits=16, scale=None, stream=None, o_part=None,
+                  lse_part=None):
+    """fwd_splitkv_varlen followed by the combine: O [B, H, 1, d], LSE [B, H, 1]."""
+    o_part, lse_part = fwd_splitkv_varlen(q, k, v, cu_seqlens_k, max_seqlen_k, num_splits, scale, o_part,
+                                          lse_part, stream)
     return splitkv_combine(o_part, lse_part, q.dtype, stream=stream)
 
 

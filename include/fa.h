@@ -181,6 +181,34 @@ fa_status fa_fwd_splitkv_paged(const void* q, const void* k_cache, const void* v
                                float scale, int num_splits, fa_dtype dtype, void* stream);
 
 /*
+ * Split-KV decode over packed variable-length sequences: one query row per
+ * sequence and head (q [B, H, d], i.e. the packed query layout [total_q, H, d]
+ * with one row per sequence) attending to that sequence's keys, which are
+ * stored back to back without padding and located by cumulative offsets (Ringi,
+ * "Lecture 25", section 7: the varlen interface; LLM Infra Atlas, "FA2:
+ * parallelism", section 2: split-KV for decode).
+ *   k, v          [total_k, H_kv, d]  dtype, 16-byte aligned; sequence b owns
+ *                 rows [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ *   cu_seqlens_k  [B + 1]  int32, device, 4-byte aligned
+ * Query head h reads K/V head h / (H / H_kv).  The query row sees every key of
+ * its sequence (bottom-right causal alignment puts a single query row after all
+ * its keys, so causal and non-causal coincide).  Sequence b is split into
+ * num_splits chunks of c_b = ceil(len_b / num_splits) keys as in
+ * fa_fwd_splitkv_paged; the outputs are the partials of fa_fwd_splitkv with
+ * Nq = 1 (o_part [num_splits, B, H, 1, d], lse_part [num_splits, B, H, 1]),
+ * merged by fa_splitkv_combine.  A sequence of length 0 gives O = 0 and
+ * LSE = -inf.  Requirements: H % H_kv == 0, num_splits >= 1,
+ * 1 <= max_seqlen_k <= total_k.  The offsets live on the device and are not
+ * read by the host: a sequence whose offsets leave [0, total_k], decrease or
+ * span more than max_seqlen_k keys leaves its partials as the caller's buffers
+ * held them; no memory outside the tensors is accessed.
+ */
+fa_status fa_fwd_splitkv_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens_k,
+                                float* o_part, float* lse_part,
+                                int B, int H, int H_kv, int total_k, int max_seqlen_k, int d,
+                                float scale, int num_splits, fa_dtype dtype, void* stream);
+
+/*
  * FP8 forward (Ringi, "Lecture 25", section 5.4: Q K^T and P V on FP8 operands
  * with per-block scale factors): O and LSE of attention on the dequantized
  * inputs x = code * descale, where

@@ -213,6 +213,32 @@ def paged(q=A, kc=A, vc=A, bt=A, sl=A, op=A, lp=A, B=2, H=4, H_kv=2, d=128, ps=1
                                          scale, S, dtype, NULL)
 
 
+def split_varlen(q=A, k=A, v=A, ck=A, op=A, lp=A, B=3, H=8, H_kv=2, total_k=100, max_k=60, d=128, scale=0.1,
+                 S=4, dtype=0):
+    return fa.lib().fa_fwd_splitkv_varlen(q, k, v, ck, op, lp, B, H, H_kv, total_k, max_k, d, scale, S, dtype,
+                                          NULL)
+
+
+def test_splitkv_varlen_validation():
+    for kw in ("q", "k", "v", "ck", "op", "lp"):
+        assert split_varlen(**{kw: NULL}) == fa.FA_ERR_NULL, kw
+    assert split_varlen(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert split_varlen(dtype=5) == fa.FA_ERR_UNSUPPORTED
+    assert split_varlen(scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
+    assert split_varlen(H=6, H_kv=4) == fa.FA_ERR_SHAPE
+    assert split_varlen(H_kv=0) == fa.FA_ERR_SHAPE
+    assert split_varlen(B=0) == fa.FA_ERR_SHAPE
+    assert split_varlen(S=0) == fa.FA_ERR_SHAPE
+    assert split_varlen(total_k=0) == fa.FA_ERR_SHAPE
+    assert split_varlen(max_k=0) == fa.FA_ERR_SHAPE
+    assert split_varlen(max_k=101) == fa.FA_ERR_SHAPE       # longer than all keys together
+    assert split_varlen(B=1 << 20, H=1 << 12, H_kv=1 << 12) == fa.FA_ERR_SHAPE   # B * H past int32
+    assert split_varlen(q=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert split_varlen(v=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert split_varlen(op=MIS) == fa.FA_ERR_UNSUPPORTED
+    assert split_varlen(ck=ctypes.c_void_p(0x10002)) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_paged_validation():
     for kw in ("q", "kc", "vc", "bt", "sl", "op", "lp"):
         assert paged(**{kw: NULL}) == fa.FA_ERR_NULL, kw

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from exact_attention_22_amd import fa
-from exact_attention_22_amd.inputs import BY_NAME, make_paged
+from exact_attention_22_amd.inputs import BY_NAME, make_paged, make_varlen_decode
 from oracle import fp8 as ofp8
 
 pytestmark = pytest.mark.gpu
@@ -94,6 +94,16 @@ def test_canary_paged(dev):
     op, lp = Padded((S, 3, 8, 1, w.d), torch.float32, dev), Padded((S, 3, 8, 1), torch.float32, dev)
     fa.fwd_splitkv_paged(q, kc, vc, bt, sl, S, o_part=op.view, lse_part=lp.view)
     check([op, lp], fa.fwd_splitkv_paged(q, kc, vc, bt, sl, S), "paged partials")
+
+
+def test_canary_packed_decode(dev):
+    w = BY_NAME["decode_varlen"].with_(H=8, H_kv=2, seed=91)
+    q, k, v, cu = (t.to(dev) for t in make_varlen_decode(w, seqlens=[300, 1, 0, 77], spare_rows=3))
+    S = 5
+    say("canary fa_fwd_splitkv_varlen")
+    op, lp = Padded((S, 4, 8, 1, w.d), torch.float32, dev), Padded((S, 4, 8, 1), torch.float32, dev)
+    fa.fwd_splitkv_varlen(q, k, v, cu, 300, S, o_part=op.view, lse_part=lp.view)
+    check([op, lp], fa.fwd_splitkv_varlen(q, k, v, cu, 300, S), "packed decode partials")
 
 
 def test_canary_fwd_gqa_and_varlen(dev):
