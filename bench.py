@@ -136,6 +136,29 @@ def host_cores():
     return use, host, affinity, quota
 
 
+def hbm_copy_rate(dev, stream, mib=1024, reps=10):
+    """Device-to-device copy of `mib` MiB by torch, timed with HIP events on the
+    stream: a measured ceiling for the streaming (decode) kernels, counted as
+    read + write bytes."""
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    moved = 2 * n * 4
+    del src, dst
+    gbs = moved / (ms * 1e-3) / 1e9
+    return {"GB_per_s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, "bytes_per_copy": moved, "us_per_copy": ms * 1e3,
+            "what": f"torch device-to-device copy of {mib} MiB, read + write bytes, mean of {reps}"}
+
+
 def cpu_baseline(q, k, v, w, target_rows):
     """Time the fp64 oracle on evenly spaced rows of the prefill workload."""
     import numpy as np
@@ -477,6 +500,8 @@ def main():
             out.update({"value": t8, "unit": "TFLOP/s", "dtype": "fp8"})
             cfg["workload"] = "fp8 on long_causal: B=1 H=32 Nq=Nk=8192 d=128 e4m3 causal"
     out["config"] = cfg
+    if any(on[x] for x in ("decode", "decode_gqa", "decode_paged", "decode_varlen")):
+        out["hbm_copy"] = hbm_copy_rate(dev, stream)
     if on["prefill"] and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(q, k, v, wp, args.cpu_rows)
     print(json.dumps(out), flush=True)
