@@ -391,19 +391,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
         if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // masked tiles: per-wave visibility checks, stage chosen at run time
+        // masked tiles: per-wave visibility checks, two per trip so that each step
+        // reads one fixed stage (with the stage chosen at run time the compiler
+        // cannot tell the stage being read from the one being filled, and waits
+        // for the next tile's loads in the middle of the step)
         int it = 0;
-    #pragma clang loop unroll(disable)
-        for (; it < n_masked; ++it) {
+        auto masked_step = [&](unsigned char* cur, unsigned char* nxt) {
             const int tile = n_tiles - 1 - it;
-            unsigned char* cur = (it & 1) ? stage1 : stage0;
-            unsigned char* nxt = (it & 1) ? stage0 : stage1;
             if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
             const int k0 = ks + tile * BC;
             const bool active = qw < Nq && (!CAUSAL || k0 <= qmax_w + off);
             if (active) key_tile(cur, cur + TILE, k0, std::true_type{}, [] {});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            ++it;
+        };
+    #pragma clang loop unroll(disable)
+        while (it < n_masked) {
+            masked_step(stage0, stage1);
+            if (it < n_masked) masked_step(stage1, stage0);
         }
         // clean tiles, two per trip so that each half reads one fixed stage.  The
         // next tile's K loads go out at the start of the step and its V loads after
@@ -493,23 +499,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
         const int len = a.cu_q[b + 1] - a.cu_q[b];     // run_item checks the offsets themselves
         const int nb = (len > 0 && len <= a.max_q) ? (len + BR - 1) / BR : 0;
         if (t < ((nb + 1) >> 1)) {
-            run_item(nb - 1 - t, bh, 0);
-            if (t != nb - 1 - t) {
-                __syncthreads();    // the next item refills stage0
-                run_item(t, bh, 0);
+            // the two items run through one copy of the item code (a loop, not two
+            // inlined calls), which keeps the kernel small for the instruction cache
+    #pragma clang loop unroll(disable)
+            for (int r = 0; r < 2; ++r) {
+                if (r == 1) {
+                    if (t == nb - 1 - t) break;
+                    __syncthreads();    // the next item refills stage0
+                }
+                run_item(r == 0 ? nb - 1 - t : t, bh, 0);
             }
         }
-    } else if (CAUSAL && !VARLEN && !SPLIT && a.paired) {
+    } else if constexpr (CAUSAL && !VARLEN && !SPLIT) {
         // Causal query tiles t and n_qtiles-1-t together see a fixed number of key
         // tiles, so pairing them gives every workgroup the same work: the
         // round-robin dispatcher then never waits on one XCD's long tile while
-        // another XCD has free slots.
+        // another XCD has free slots.  (A single query tile is the pair t = 0.)
         const int npairs = (a.n_qtiles + 1) >> 1;
         const int t = L % npairs, bh = L / npairs;
-        run_item(a.n_qtiles - 1 - t, bh, 0);
-        if (t != a.n_qtiles - 1 - t) {
-            __syncthreads();        // the next item refills stage0
-            run_item(t, bh, 0);
+    #pragma clang loop unroll(disable)
+        for (int r = 0; r < 2; ++r) {
+            if (r == 1) {
+                if (t == a.n_qtiles - 1 - t) break;
+                __syncthreads();        // the next item refills stage0
+            }
+            run_item(r == 0 ? a.n_qtiles - 1 - t : t, bh, 0);
         }
     } else {
         const int rest = L / a.n_qtiles;
@@ -578,7 +592,7 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     a.max_k = p.Nk;
     // causal [B,H,N,d]: one workgroup per pair of query tiles (two pairs per
     // workgroup, one dispatch round with no rebalancing, measured slower)
-    a.paired = (p.causal && mode == 0 && a.n_qtiles >= 2) || (mode == 2 && (a.B * a.H_kv) % 8 == 0);
+    a.paired = (p.causal && mode == 0) || (mode == 2 && (a.B * a.H_kv) % 8 == 0);
     const int64_t blocks = a.paired ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH : (int64_t)a.n_qtiles * a.BH * S;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.d == 128)
