@@ -13,6 +13,7 @@ One step = one pass of the whole path over resident synthetic inputs:
     keys (decode_varlen: lengths log-uniform in [512, 32768], 129054 keys, the
     32 query heads on 8 K/V heads, 16 splits per sequence), and
   * bwd: fa_bwd on the long-context causal workload (dO ~ N(0,1)), and
+    bwd_varlen: fa_bwd_varlen on the packed varlen_gqa sequences, and
   * fp8: fa_fwd_fp8 on the long-context workload's inputs quantized to e4m3
     per block (quantized once, untimed), and
   * varlen: fa_fwd_varlen on 16 packed causal sequences (lengths log-uniform in
@@ -189,7 +190,7 @@ def stats_us(times_ms):
 
 
 LEGS = ["prefill", "prefill_d64", "causal_d128", "decode", "decode_gqa", "decode_paged", "decode_varlen", "varlen",
-        "bwd", "fp8"]
+        "bwd", "bwd_varlen", "fp8"]
 
 
 def main():
@@ -280,6 +281,18 @@ def main():
         vmax = max(wv.seqlens)
         calls["varlen"] = [("fwd", lambda: fa.fwd_varlen(vq, vk, vv, vcq, vck, vmax, vmax, causal=wv.causal,
                                                          scale=wv.scale, out=vo, lse=vlse, stream=stream))]
+    if on["bwd_varlen"]:
+        bvq, bvk, bvv, bvcq, bvck = make_varlen(wv, device=dev)
+        bvmax = max(wv.seqlens)
+        bvo, bvlse = fa.fwd_varlen(bvq, bvk, bvv, bvcq, bvck, bvmax, bvmax, causal=wv.causal, scale=wv.scale)
+        gen_v = torch.Generator(device=dev)
+        gen_v.manual_seed(wv.seed + 100)
+        bvdo = torch.randn(tuple(bvq.shape), generator=gen_v, device=dev, dtype=torch.float32).to(wv.dtype)
+        bvdq, bvdk, bvdv = torch.empty_like(bvq), torch.empty_like(bvk), torch.empty_like(bvv)
+        bvws = torch.empty(fa.bwd_workspace_bytes(1, wv.H, bvq.shape[0]) // 4, dtype=torch.float32, device=dev)
+        calls["bwd_varlen"] = [("bwd", lambda: fa.bwd_varlen(bvq, bvk, bvv, bvo, bvlse, bvdo, bvcq, bvck, bvmax, bvmax,
+                                                             causal=wv.causal, scale=wv.scale, dq=bvdq, dk=bvdk,
+                                                             dv=bvdv, workspace=bvws, stream=stream))]
     if on["bwd"]:
         fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, out=o, lse=lse)
         gen = torch.Generator(device=dev)
@@ -485,6 +498,20 @@ def main():
         if args.only == "bwd":
             out.update({"value": tb, "unit": "TFLOP/s", "dtype": "bf16"})
             cfg["workload"] = "bwd on long_causal: B=1 H=32 Nq=Nk=8192 d=128 bf16 causal"
+    if on["bwd_varlen"]:
+        fl = 2.5 * sum(attn_flops(1, wv.H, n, n, wv.d, wv.causal) for n in wv.seqlens)
+        t_bv = leg_ms("bwd_varlen", mean)
+        tbv = fl / (t_bv * 1e-3) / 1e12
+        out["bwd_varlen"] = {"TFLOP_per_s": tbv, "pct_mfma_peak": 100.0 * tbv / PEAK_TFLOPS, "flop_per_launch": fl,
+                             **stats_us(times[("bwd_varlen", "bwd")])}
+        out["roofline_bwd_varlen"] = {"bound": "mfma", "achieved": tbv, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": tbv / PEAK_TFLOPS, "traffic": None,
+                                      "kernel": "bwd_delta + bwd_dkdv + bwd_dq <bf16, d=128, causal, varlen>"}
+        cfg["bwd_varlen"] = {"sequences": wv.B, "tokens": sum(wv.seqlens), "max_seqlen": max(wv.seqlens),
+                             "H": wv.H, "H_kv": wv.H_kv, "d": wv.d, "dtype": "bf16", "causal": True}
+        if args.only == "bwd_varlen":
+            out.update({"value": tbv, "unit": "TFLOP/s", "dtype": "bf16"})
+            cfg["workload"] = "bwd_varlen on varlen_gqa: 16 packed causal sequences, 20752 tokens, H=32 H_kv=8"
     if on["fp8"]:
         fl = attn_flops(wp.B, wp.H, wp.Nq, wp.Nk, wp.d, wp.causal)
         t_f8 = leg_ms("fp8", mean)
