@@ -54,7 +54,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int F8_D = 128;       // head dimension (bytes per row)
-constexpr int F8_BR = 128;      // query rows per workgroup (4 waves x 32) = Q scale block
+constexpr int F8_QB = 128;      // query rows per Q scale block
 constexpr int F8_BC = 128;      // keys per tile = K scale block
 constexpr float F8_TAU = 4.0f;  // lazy-rescale threshold, log2 units
 constexpr float F8_LIFT = 4.0f; // P lift, log2 units (TAU + LIFT <= log2(448))
@@ -69,6 +69,7 @@ struct F8Args {
     uint16_t* o;       // bf16 [B, H, Nq, d]
     float* lse;        // [B, H, Nq]
     int B, H, H_kv, group, Nq, Nk, BH, n_qtiles, n_kblk;
+    int n_qblk;        // Q scale blocks per head: ceil(Nq / 128)
     float c;           // |scale| * log2(e)
     u32 qsign;         // 0x80808080 flips Q's sign when scale < 0
 };
@@ -98,10 +99,13 @@ __device__ __forceinline__ int pack4_f8(float x0, float x1, float x2, float x3) 
     return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
+// NW wavefronts per workgroup, 32 query rows each: 4 (two workgroups per CU) or 8
+// (one per CU; each K/V tile is then loaded once for 256 query rows)
+template <bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(F8Args a) {
+    constexpr int BR = 32 * NW;                 // query rows per workgroup
     constexpr int TILE = F8_BC * F8_D;          // 16 KiB per K or V tile
-    constexpr int NPW = TILE / 1024 / 4;        // 1 KiB loads per wave per tensor per tile
+    constexpr int NPW = TILE / 1024 / NW;       // 1 KiB loads per wave per tensor per tile
     constexpr int ND = F8_D / 32;               // 32-wide d blocks of O^T
     __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];   // [K | V]
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
     if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
     auto run_item = [&](const int qt, const int bh) __attribute__((always_inline)) {
         const int bkv = (bh / a.H) * a.H_kv + (bh % a.H) / a.group;
-        const int q0 = qt * F8_BR;
+        const int q0 = qt * BR;
         const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
 
         const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,11 +128,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
         const uint8_t* qg = a.q + (size_t)bh * Nq * F8_D;
         const uint8_t* kg = a.k + (size_t)bkv * Nk * F8_D;
         const uint8_t* vg = a.v + (size_t)bkv * Nk * F8_D;
-        const float cq = a.c * a.qd[(size_t)bh * a.n_qtiles + qt];
+        const float cq = a.c * a.qd[(size_t)bh * a.n_qblk + (q0 + 32 * w) / F8_QB];   // this wave's Q block
         const float* kdh = a.kd + (size_t)bkv * a.n_kblk;
 
         int hi = Nk;
-        if (CAUSAL) hi = min(hi, min(Nq, q0 + F8_BR) + off);
+        if (CAUSAL) hi = min(hi, min(Nq, q0 + BR) + off);
         const int n_tiles = hi > 0 ? (hi + F8_BC - 1) / F8_BC : 0;
 
         // Q: bytes 64ks + 32h .. +31 of this lane's row, for ks = 0, 1
@@ -281,23 +285,37 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
         if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // two tiles per trip, so that each step reads one fixed LDS stage
-        auto one = [&](int it, unsigned char* cur, unsigned char* nxt) {
+        // the masked tiles, then the clean ones, each two per trip so that every step
+        // reads one fixed LDS stage (one body per loop: nothing meets at a branch join,
+        // and the compiler can tell the stage being read from the one being filled)
+        int it = 0;
+        auto masked_step = [&](unsigned char* cur, unsigned char* nxt) {
             const int tile = n_tiles - 1 - it;
             if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
-            if (it < n_masked) {
-                const int k0 = tile * F8_BC;
-                if (qw < Nq && (!CAUSAL || k0 <= qmax_w + off)) tile_step(cur, cur + TILE, tile, std::true_type{});
-            } else {
-                tile_step(cur, cur + TILE, tile, std::false_type{});
-            }
+            const int k0 = tile * F8_BC;
+            if (qw < Nq && (!CAUSAL || k0 <= qmax_w + off)) tile_step(cur, cur + TILE, tile, std::true_type{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            ++it;
+        };
+        auto clean_step = [&](unsigned char* cur, unsigned char* nxt) {
+            const int tile = n_tiles - 1 - it;
+            if (it + 1 < n_tiles) load_tile(tile - 1, nxt);
+            tile_step(cur, cur + TILE, tile, std::false_type{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            ++it;
         };
     #pragma clang loop unroll(disable)
-        for (int it = 0; it < n_tiles; it += 2) {
-            one(it, stage0, stage1);
-            if (it + 1 < n_tiles) one(it + 1, stage1, stage0);
+        while (it < n_masked) {
+            masked_step(stage0, stage1);
+            if (it < n_masked) masked_step(stage1, stage0);
+        }
+        if ((it & 1) && it < n_tiles) clean_step(stage1, stage0);
+    #pragma clang loop unroll(disable)
+        while (it < n_tiles) {
+            clean_step(stage0, stage1);
+            if (it < n_tiles) clean_step(stage1, stage0);
         }
 
         // epilogue: O = vd * O_acc / l (bf16); LSE = (M + log2 l - LIFT) ln 2
@@ -317,13 +335,18 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
             if (h == 0) a.lse[(size_t)bh * Nq + qi] = lse_v;
         }
     };
-    if (CAUSAL && a.n_qtiles >= 2) {
+    if constexpr (CAUSAL) {
+        // the two items run through one copy of the item code (a single query tile
+        // is the pair t = 0)
         const int npairs = (a.n_qtiles + 1) >> 1;
         const int t = L % npairs, bh = L / npairs;
-        run_item(a.n_qtiles - 1 - t, bh);
-        if (t != a.n_qtiles - 1 - t) {
-            __syncthreads();        // the next item refills stage0
-            run_item(t, bh);
+    #pragma clang loop unroll(disable)
+        for (int r = 0; r < 2; ++r) {
+            if (r == 1) {
+                if (t == a.n_qtiles - 1 - t) break;
+                __syncthreads();        // the next item refills stage0
+            }
+            run_item(r == 0 ? a.n_qtiles - 1 - t : t, bh);
         }
     } else {
         run_item(a.n_qtiles - 1 - (L % a.n_qtiles), (L / a.n_qtiles) % a.BH);
@@ -391,17 +414,23 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream) {
     a.Nq = p.Nq;
     a.Nk = p.Nk;
     a.BH = p.B * p.H;
-    a.n_qtiles = (p.Nq + F8_BR - 1) / F8_BR;
+    // 8 wavefronts (256 query rows per workgroup) over long key ranges
+    const bool wide = p.Nk >= 4096;
+    const int br = wide ? 256 : 128;
+    a.n_qtiles = (p.Nq + br - 1) / br;
+    a.n_qblk = (p.Nq + F8_QB - 1) / F8_QB;
     a.n_kblk = (p.Nk + F8_BC - 1) / F8_BC;
     a.c = fabsf(p.scale) * kLog2e;
     a.qsign = p.scale < 0.f ? 0x80808080u : 0u;
-    const int64_t blocks = (p.causal && a.n_qtiles >= 2) ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH
-                                                         : (int64_t)a.n_qtiles * a.BH;
+    const int64_t blocks = p.causal ? (int64_t)((a.n_qtiles + 1) / 2) * a.BH : (int64_t)a.n_qtiles * a.BH;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (p.causal)
-        hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3((int)blocks), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((fwd_fp8_kernel<false>), dim3((int)blocks), dim3(256), 0, stream, a);
+    if (p.causal) {
+        if (wide) hipLaunchKernelGGL((fwd_fp8_kernel<true, 8>), dim3((int)blocks), dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((fwd_fp8_kernel<true, 4>), dim3((int)blocks), dim3(256), 0, stream, a);
+    } else {
+        if (wide) hipLaunchKernelGGL((fwd_fp8_kernel<false, 8>), dim3((int)blocks), dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((fwd_fp8_kernel<false, 4>), dim3((int)blocks), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
