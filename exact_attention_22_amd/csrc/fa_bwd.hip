@@ -44,7 +44,7 @@
 namespace fa {
 namespace {
 
-constexpr int BQ = 128;   // dQ kernel: query rows per workgroup (4 waves x 32)
+constexpr int BQ = 128;   // dQ kernel: query rows per workgroup of 4 waves (32 each)
 constexpr int BK = 64;    // dQ kernel: keys per tile
 constexpr int CK = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int CQ = 64;    // dK/dV kernel: query rows per tile
@@ -329,10 +329,13 @@ __device__ __forceinline__ void dq_accum(const unsigned char* Kb, int kb, const 
     }
 }
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+// NW wavefronts of 32 query rows: 4 (two workgroups per CU) or 8 (one per CU;
+// each K/V tile is then loaded once for 256 rows)
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
     constexpr int ROWB = D * 2, TILE = BK * ROWB, NS = D / 16, ND = D / 32;
-    constexpr int NPW = TILE / 1024 / 4;
+    constexpr int BQW = 32 * NW;                 // query rows per workgroup
+    constexpr int NPW = TILE / 1024 / NW;
     __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * TILE];   // [K | V]
     __shared__ __attribute__((aligned(16))) unsigned char stage1[2 * TILE];
 
@@ -340,16 +343,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         const int bkv = a.group == 1 ? bh : (bh / a.H) * a.H_kv + (bh % a.H) / a.group;   // K/V head read
         const Seq sg = seq_of<D, VARLEN>(a, bh, bkv);
         const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
-        const int nqt = VARLEN ? (Nq + BQ - 1) / BQ : a.n_qtiles;
+        const int nqt = VARLEN ? (Nq + BQW - 1) / BQW : a.n_qtiles;
         if (VARLEN && (!sg.ok || t >= nqt)) return;      // past this sequence's rows
         const int qt = nqt - 1 - t;                      // longest causal rows first
         const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, h = lane >> 5;
-        const int q0 = qt * BQ, qw = q0 + 32 * w, qi = qw + l32;
+        const int q0 = qt * BQW, qw = q0 + 32 * w, qi = qw + l32;
         const uint16_t* kg = a.k + sg.k;
         const uint16_t* vg = a.v + sg.k;
 
         int hi = Nk;
-        if (CAUSAL) hi = min(hi, min(Nq, q0 + BQ) + off);
+        if (CAUSAL) hi = min(hi, min(Nq, q0 + BQW) + off);
         const int n_tiles = hi > 0 ? (hi + BK - 1) / BK : 0;
 
         // this lane's query row: Q and dO chunks, LSE (log2 units) and D
@@ -440,8 +443,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
 
         // the walk ended with a barrier, so the stages are free: each wave stages
-        // its 32 rows in its own quarter of stage 0
-        store_rows_staged<BF16, D>(dqacc, a.scale, stage0 + w * (32 * ROWB), a.dq + sg.q, sg.sq, qw, Nq, lane);
+        // its 32 rows in its own quarter of stage 0 (waves 4..7: of stage 1)
+        store_rows_staged<BF16, D>(dqacc, a.scale, (w < 4 ? stage0 : stage1) + (w & 3) * (32 * ROWB), a.dq + sg.q,
+                                   sg.sq, qw, Nq, lane);
     };
     for_items<CAUSAL, !VARLEN>(a.n_qtiles, a.BH, run_item);
 }
@@ -709,18 +713,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for_items<CAUSAL, !VARLEN>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
 }
 
+// 8-wavefront dQ workgroups for dense d = 128 over long key ranges
+inline bool dq_wide(bool varlen, int d, int Nk) { return !varlen && d == 128 && Nk >= 4096; }
+
 template <bool BF16, int D, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
     const int64_t dblocks = (rows + 255) / 256;
     hipLaunchKernelGGL((bwd_delta_kernel<BF16, D, VARLEN>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
     const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH / a.group);
     const int q_blocks = (int)item_blocks(causal, a.n_qtiles, a.BH);
+    const bool wide = dq_wide(VARLEN, D, a.Nk);
     if (causal) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true, VARLEN>), dim3(kv_blocks), dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, VARLEN>), dim3(q_blocks), dim3(256), 0, s, a);
+        if constexpr (D == 128 && !VARLEN)
+            if (wide) {
+                hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, VARLEN, 8>), dim3(q_blocks), dim3(512), 0, s, a);
+                return hipGetLastError();
+            }
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, VARLEN, 4>), dim3(q_blocks), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, false, VARLEN>), dim3(kv_blocks), dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, VARLEN>), dim3(q_blocks), dim3(256), 0, s, a);
+        if constexpr (D == 128 && !VARLEN)
+            if (wide) {
+                hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, VARLEN, 8>), dim3(q_blocks), dim3(512), 0, s, a);
+                return hipGetLastError();
+            }
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, VARLEN, 4>), dim3(q_blocks), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
@@ -763,7 +781,8 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.Nk = p.Nk;
     a.c = p.scale * kLog2e;
     a.scale = p.scale;
-    a.n_qtiles = (p.Nq + BQ - 1) / BQ;
+    const int bq = dq_wide(varlen, p.d, p.Nk) ? 2 * BQ : BQ;
+    a.n_qtiles = (p.Nq + bq - 1) / bq;
     a.n_ktiles = (p.Nk + CK - 1) / CK;
     if ((int64_t)a.n_qtiles * a.BH > 0x7fffffff || (int64_t)a.n_ktiles * a.BH > 0x7fffffff ||
         (rows + 255) / 256 > 0x7fffffff)
