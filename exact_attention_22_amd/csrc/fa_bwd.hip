@@ -123,32 +123,53 @@ __device__ __forceinline__ int perm_row(int i) {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// D_i = sum_t dO[i,t] O[i,t] in fp32, and LSE_i * log2(e), one thread per row.
-// Packed sequences: thread row = h * total_q + i reads O row (i, h).
+// D_i = sum_t dO[i,t] O[i,t] in fp32, and LSE_i * log2(e).  A row's D 16-bit
+// values are spread over D/8 lanes, 16 bytes each, so every wave load reads whole
+// rows of consecutive memory; the lanes' partial sums are added by a fixed xor
+// butterfly.  Each wave handles DELTA_U groups of 64/(D/8) rows, their loads
+// issued together.  Packed sequences: row = h * total_q + i reads O row (i, h).
+constexpr int DELTA_U = 4;
+template <int D>
+constexpr int delta_rows_per_block() { return 4 * (64 / (D / 8)) * DELTA_U; }
+
 template <bool BF16, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t rows) {
-    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (row >= rows) return;
-    size_t orow = (size_t)row;
-    if constexpr (VARLEN) {
-        const int64_t h = row / a.total_q;
-        orow = (size_t)(row - h * a.total_q) * a.H + (size_t)h;
-    }
-    const uint16_t* op = a.o + orow * D;
-    const uint16_t* gp = a.dout + orow * D;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int t = 0; t < D; t += 8) {
-        const u32x4 ov = *(const u32x4*)(op + t);
-        const u32x4 gv = *(const u32x4*)(gp + t);
+    constexpr int CH = D / 8, RPW = 64 / CH;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane % CH, r = lane / CH;
+    int64_t row[DELTA_U];
+    u32x4 ov[DELTA_U], gv[DELTA_U];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = __builtin_fmaf(widen<BF16>((uint16_t)(ov[i] & 0xffff)), widen<BF16>((uint16_t)(gv[i] & 0xffff)), acc);
-            acc = __builtin_fmaf(widen<BF16>((uint16_t)(ov[i] >> 16)), widen<BF16>((uint16_t)(gv[i] >> 16)), acc);
+    for (int u = 0; u < DELTA_U; ++u) {
+        row[u] = (int64_t)blockIdx.x * delta_rows_per_block<D>() + (u * 4 + w) * RPW + r;
+        size_t orow = (size_t)row[u];
+        if constexpr (VARLEN) {
+            const int64_t h = row[u] / a.total_q;
+            orow = (size_t)(row[u] - h * a.total_q) * a.H + (size_t)h;
+        }
+        if (row[u] < rows) {
+            ov[u] = *(const u32x4*)(a.o + orow * D + 8 * c);
+            gv[u] = *(const u32x4*)(a.dout + orow * D + 8 * c);
+        } else {
+            ov[u] = u32x4{0, 0, 0, 0};
+            gv[u] = u32x4{0, 0, 0, 0};
         }
     }
-    a.delta[row] = acc;
-    a.lse2[row] = a.lse[row] * kLog2e;
+#pragma unroll
+    for (int u = 0; u < DELTA_U; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(widen<BF16>((uint16_t)(ov[u][i] & 0xffff)), widen<BF16>((uint16_t)(gv[u][i] & 0xffff)),
+                                 acc);
+            acc = __builtin_fmaf(widen<BF16>((uint16_t)(ov[u][i] >> 16)), widen<BF16>((uint16_t)(gv[u][i] >> 16)), acc);
+        }
+#pragma unroll
+        for (int m = 1; m < CH; m <<= 1) acc += __shfl_xor(acc, m);
+        if (c == 0 && row[u] < rows) {
+            a.delta[row[u]] = acc;
+            a.lse2[row[u]] = a.lse[row[u]] * kLog2e;
+        }
+    }
 }
 
 // Per-lane LDS offsets shared by both kernels (tiles of rows of D 16-bit values,
@@ -718,7 +739,7 @@ inline bool dq_wide(bool varlen, int d, int Nk) { return !varlen && d == 128 && 
 
 template <bool BF16, int D, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
-    const int64_t dblocks = (rows + 255) / 256;
+    const int64_t dblocks = (rows + delta_rows_per_block<D>() - 1) / delta_rows_per_block<D>();
     hipLaunchKernelGGL((bwd_delta_kernel<BF16, D, VARLEN>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
     const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH / a.group);
     const int q_blocks = (int)item_blocks(causal, a.n_qtiles, a.BH);
@@ -785,7 +806,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.n_qtiles = (p.Nq + bq - 1) / bq;
     a.n_ktiles = (p.Nk + CK - 1) / CK;
     if ((int64_t)a.n_qtiles * a.BH > 0x7fffffff || (int64_t)a.n_ktiles * a.BH > 0x7fffffff ||
-        (rows + 255) / 256 > 0x7fffffff)
+        (rows + delta_rows_per_block<128>() - 1) / delta_rows_per_block<128>() > 0x7fffffff)
         return hipErrorInvalidValue;
     return varlen ? launch_bwd_v<true>(a, p.d, p.bf16, p.causal, rows, stream)
                   : launch_bwd_v<false>(a, p.d, p.bf16, p.causal, rows, stream);
