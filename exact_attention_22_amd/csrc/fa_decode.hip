@@ -180,40 +180,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
     }
 
-    // page entries of the first step (paged)
-    int pnext[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) pnext[u] = PAGED ? page_of(ks + (w + 4 * u) * KPI + r) : 0;
-
-    for (int g0 = w; g0 < ngroups; g0 += 4 * U) {
-        u32x4 kr[U], vr[U];
-        int key[U];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            key[u] = ks + (g0 + 4 * u) * KPI + r;
-            size_t row;
-            if constexpr (PAGED) {
-                // a page entry outside [0, num_pages) drops its keys
-                const int pg = pnext[u];
-                ok[u] = key[u] < ke && (unsigned)pg < (unsigned)a.num_pages;
-                row = (((size_t)pg << a.page_shift) + (key[u] & ((1 << a.page_shift) - 1))) * a.H_kv + hk;
-            } else {
-                ok[u] = key[u] < ke;
-                row = KV == KV_PACKED ? (size_t)key[u] * a.H_kv : (size_t)key[u];
-            }
-            if (ok[u]) {
-                kr[u] = *(const u32x4*)(kg + row * D + 8 * c);
-                vr[u] = *(const u32x4*)(vg + row * D + 8 * c);
-            } else {
-                kr[u] = u32x4{0, 0, 0, 0};
-                vr[u] = u32x4{0, 0, 0, 0};
-            }
-        }
-        if constexpr (PAGED) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) pnext[u] = page_of(key[u] + 4 * U * KPI);   // next step's keys
-        }
+    // One step's scores, online-softmax update and P V accumulation over the U
+    // key groups in registers; a key that does not exist (ok false) scores -inf
+    // and its K and V values are zeros.
+    auto consume = [&](const u32x4* kr, const u32x4* vr, const bool* ok) {
         float s[GP][U];
         float mx[GP];
 #pragma unroll
@@ -250,6 +220,79 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(p, vf[i], acc[g][i]);
             }
+        }
+    };
+
+    // Paged keys whose groups never straddle a page (the split starts at a
+    // multiple of KPI and a page holds a multiple of KPI rows): the KPI keys of a
+    // wave load share one page, so its entry is one scalar load and its row base
+    // scalar arithmetic, and the rows come through a buffer resource that ends
+    // with the group's last key before the split's end (no records for an
+    // invalid page), so a lane's offset is a constant and absent rows read as
+    // zeros.  This takes the per-lane page lookup and 64-bit row arithmetic out
+    // of the vector work (decode_paged 219.8 -> 214.4 us, same partials).  With
+    // one query head per workgroup the extra registers would cost a wavefront
+    // per SIMD, so that case keeps the per-lane path.
+    const int pmask = (1 << a.page_shift) - 1;
+    if (PAGED && GP >= 2 && (ks % KPI) == 0 && ((pmask + 1) % KPI) == 0) {
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const int ksu = __builtin_amdgcn_readfirstlane(ks), keu = __builtin_amdgcn_readfirstlane(ke);
+        const u32 lo = (u32)((r * a.H_kv * D + 8 * c) * 2);
+        for (int g0 = wu; g0 < ngroups; g0 += 4 * U) {
+            u32x4 kr[U], vr[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kf = ksu + (g0 + 4 * u) * KPI;              // the group's first key
+                const int pg = kf < keu ? __builtin_amdgcn_readfirstlane(bt[kf >> a.page_shift]) : -1;
+                const bool pok = (unsigned)pg < (unsigned)a.num_pages;
+                const int nrows = pok ? min(KPI, keu - kf) : 0;
+                ok[u] = pok && kf + r < keu;
+                const size_t rowb = (((size_t)(pok ? pg : 0) << a.page_shift) + (kf & pmask)) * a.H_kv + hk;
+                const u32 nrec = nrows > 0 ? (u32)(((nrows - 1) * a.H_kv * D + D) * 2) : 0u;
+                const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + rowb * D, nrec);
+                const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + rowb * D, nrec);
+                kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lo, 0, 0));
+                vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo, 0, 0));
+            }
+            consume(kr, vr, ok);
+        }
+    } else {
+        // page entries of the first step (paged)
+        int pnext[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) pnext[u] = PAGED ? page_of(ks + (w + 4 * u) * KPI + r) : 0;
+
+        for (int g0 = w; g0 < ngroups; g0 += 4 * U) {
+            u32x4 kr[U], vr[U];
+            int key[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                key[u] = ks + (g0 + 4 * u) * KPI + r;
+                size_t row;
+                if constexpr (PAGED) {
+                    // a page entry outside [0, num_pages) drops its keys
+                    const int pg = pnext[u];
+                    ok[u] = key[u] < ke && (unsigned)pg < (unsigned)a.num_pages;
+                    row = (((size_t)pg << a.page_shift) + (key[u] & pmask)) * a.H_kv + hk;
+                } else {
+                    ok[u] = key[u] < ke;
+                    row = KV == KV_PACKED ? (size_t)key[u] * a.H_kv : (size_t)key[u];
+                }
+                if (ok[u]) {
+                    kr[u] = *(const u32x4*)(kg + row * D + 8 * c);
+                    vr[u] = *(const u32x4*)(vg + row * D + 8 * c);
+                } else {
+                    kr[u] = u32x4{0, 0, 0, 0};
+                    vr[u] = u32x4{0, 0, 0, 0};
+                }
+            }
+            if constexpr (PAGED) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) pnext[u] = page_of(key[u] + 4 * U * KPI);   // next step's keys
+            }
+            consume(kr, vr, ok);
         }
     }
 
