@@ -324,6 +324,136 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     }
 }
 
+// Paged decode with the K/V heads of one key spread over a wave load.  In the
+// cache [num_pages, page_size, H_kv, d] the rows of HG adjacent K/V heads of one
+// key are HG * 256 contiguous bytes (d = 128), where one head's consecutive keys
+// lie H_kv * 256 bytes apart.  A workgroup of 16 wavefronts takes HG = 4 K/V
+// heads (and all their query heads, GP = H / H_kv of each) of one (sequence,
+// split); a wave load reads one key for all four heads, lane row r holding head
+// hk0 + r, so every load instruction covers 1 KiB of consecutive memory.  The
+// key's page entry is one scalar load, its row base scalar arithmetic, and the
+// rows come through a buffer resource with no records for an invalid page.  Wave
+// w takes keys w, w + 16, ... of the split, so its partial state covers the keys
+// that partial w of decode_kernel covers, in the same order: the partials are
+// decode_kernel's bit for bit.  The 16 partial states per (head, query) merge
+// through LDS as there.
+template <bool BF16, int GP>
+__global__ __launch_bounds__(1024) void decode_paged_hg_kernel(DecArgs a) {
+    constexpr int D = 128, CH = 16, HG = 4, NWV = 16, U = 4;
+    __shared__ float s_m[HG][GP][NWV], s_l[HG][GP][NWV];
+    __shared__ __attribute__((aligned(16))) float s_o[HG][GP][NWV * D];
+
+    const int split = blockIdx.x % a.S;
+    const int rest = blockIdx.x / a.S;
+    const int nhg = a.H_kv / HG;
+    const int b = rest / nhg, hk0 = (rest - b * nhg) * HG;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane % CH, r = lane / CH;
+    const int len = a.seqlens[b];
+    // a length outside [0, max_pages * page_size] leaves the rows unwritten
+    if (len < 0 || len > (a.max_pages << a.page_shift)) return;
+    const int chunk = (len + a.S - 1) / a.S;
+    const int ks = __builtin_amdgcn_readfirstlane(min(len, split * chunk));
+    const int ke = __builtin_amdgcn_readfirstlane(min(len, ks + chunk));
+    const int* bt = a.block_table + (size_t)b * a.max_pages;
+    const int pmask = (1 << a.page_shift) - 1;
+    const int qh0 = b * a.H + (hk0 + r) * a.group;    // first query head of this lane's K/V head
+
+    u32x4 qp[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) qp[g] = *(const u32x4*)(a.q + (size_t)(qh0 + g) * D + 8 * c);
+    float M[GP], l[GP], acc[GP][8];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        M[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+    }
+
+    const u32 lo = (u32)((r * D + 8 * c) * 2);
+    for (int k0 = ks + w; k0 < ke; k0 += NWV * U) {
+        u32x4 kr[U], vr[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int key = k0 + NWV * u;
+            // a page entry outside [0, num_pages) drops its key
+            const int pg = key < ke ? __builtin_amdgcn_readfirstlane(bt[key >> a.page_shift]) : -1;
+            ok[u] = (unsigned)pg < (unsigned)a.num_pages;
+            const size_t rowb = (((size_t)(ok[u] ? pg : 0) << a.page_shift) + (key & pmask)) * a.H_kv + hk0;
+            const u32 nrec = ok[u] ? (u32)(HG * D * 2) : 0u;
+            const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + rowb * D, nrec);
+            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + rowb * D, nrec);
+            kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lo, 0, 0));
+            vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo, 0, 0));
+        }
+        float s[GP][U];
+        float mx[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part = dot2<BF16>(qp[g][i], kr[u][i], part);
+                s[g][u] = row_sum<CH>(part) * a.c;
+                if (!ok[u]) s[g][u] = -INFINITY;
+                mx[g] = fmaxf(mx[g], s[g][u]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            const float Mn = fmaxf(M[g], mx[g]);
+            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M[g] - Mn);
+            M[g] = Mn;
+            l[g] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+            widen8<BF16>(vr[u], vf);
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                const float p = exp2_fast(s[g][u] - ((M[g] == -INFINITY) ? 0.f : M[g]));
+                l[g] += p;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(p, vf[i], acc[g][i]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        if (c == 0) {
+            s_m[r][g][w] = M[g];
+            s_l[r][g][w] = l[g];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_o[r][g][w * D + 8 * c + i] = acc[g][i];
+    }
+    __syncthreads();
+    for (int t = tid; t < HG * GP * D; t += NWV * 64) {
+        const int hh = t / (GP * D), g = (t / D) % GP, col = t % D;
+        float Ms = -INFINITY;
+        for (int i = 0; i < NWV; ++i) Ms = fmaxf(Ms, s_m[hh][g][i]);
+        float den = 0.f, num = 0.f;
+        for (int i = 0; i < NWV; ++i) {
+            const float wgt = (s_m[hh][g][i] == -INFINITY) ? 0.f : exp2_fast(s_m[hh][g][i] - Ms);
+            den = __builtin_fmaf(wgt, s_l[hh][g][i], den);
+            num = __builtin_fmaf(wgt, s_o[hh][g][i * D + col], num);
+        }
+        const size_t row = (size_t)split * a.BH + b * a.H + (hk0 + hh) * a.group + g;
+        a.o_part[row * D + col] = den > 0.f ? num / den : 0.f;
+        if (col == 0) a.lse_part[row] = den > 0.f ? (Ms + log2f(den)) * kLn2 : -INFINITY;
+    }
+}
+
 // Max / sum over the 64 lanes of a wavefront (xor butterfly; every lane ends
 // with the result, combined in the same fixed order on every run).
 __device__ __forceinline__ float wave_max(float x) {
@@ -414,6 +544,17 @@ hipError_t launch_dec_d(const DecArgs& a, int d, bool bf16, int gp, int blocks, 
     return bf16 ? launch_dec<true, 64, KV>(a, gp, blocks, stream) : launch_dec<false, 64, KV>(a, gp, blocks, stream);
 }
 
+hipError_t launch_paged_hg(const DecArgs& a, bool bf16, int blocks, hipStream_t stream) {
+    if (a.group == 4) {
+        if (bf16) hipLaunchKernelGGL((decode_paged_hg_kernel<true, 4>), dim3(blocks), dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL((decode_paged_hg_kernel<false, 4>), dim3(blocks), dim3(1024), 0, stream, a);
+    } else {
+        if (bf16) hipLaunchKernelGGL((decode_paged_hg_kernel<true, 2>), dim3(blocks), dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL((decode_paged_hg_kernel<false, 2>), dim3(blocks), dim3(1024), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
@@ -444,6 +585,16 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
     a.cu_k = p.cu_k;
     a.total_k = p.total_k;
     a.max_k = p.Nk;
+    // a paged cache with d = 128, H_kv a multiple of 4 and 2 or 4 query heads per
+    // K/V head: four K/V heads per workgroup, one key of all four per wave load
+    // (decode_paged 213.5 -> 197.4 us, same partials).  Packed keys have the same
+    // layout but gain nothing: their time is set by the longest sequences, which
+    // workgroups four times larger balance worse (122.5 -> 124.3 us).
+    if (p.block_table && p.d == 128 && a.H_kv % 4 == 0 && (a.group == 2 || a.group == 4)) {
+        const int64_t hb = (int64_t)p.B * (a.H_kv / 4) * a.S;
+        if (hb <= 0 || hb > 0x7fffffff) return hipErrorInvalidValue;
+        return launch_paged_hg(a, p.bf16, (int)hb, stream);
+    }
     if (p.block_table) return launch_dec_d<KV_PAGED>(a, p.d, p.bf16, gp, (int)blocks, stream);
     if (p.varlen) return launch_dec_d<KV_PACKED>(a, p.d, p.bf16, gp, (int)blocks, stream);
     return launch_dec_d<KV_DENSE>(a, p.d, p.bf16, gp, (int)blocks, stream);

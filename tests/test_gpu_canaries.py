@@ -86,12 +86,13 @@ def test_canary_splitkv_and_combine(dev):
     check([op2, lp2], fa.fwd_splitkv_gqa(qg, kg, vg, S), "splitkv gqa decode partials")
 
 
-def test_canary_paged(dev):
-    w = BY_NAME["decode_paged"].with_(B=3, H=8, H_kv=2, page_size=16, seed=90)
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (16, 4)], ids=["kv2", "kv4"])
+def test_canary_paged(dev, H, H_kv):
+    w = BY_NAME["decode_paged"].with_(B=3, H=H, H_kv=H_kv, page_size=16, seed=90)
     q, kc, vc, bt, sl = (t.to(dev) for t in make_paged(w, seqlens=[300, 1, 77], spare_pages=3))
     S = 5
-    say("canary fa_fwd_splitkv_paged")
-    op, lp = Padded((S, 3, 8, 1, w.d), torch.float32, dev), Padded((S, 3, 8, 1), torch.float32, dev)
+    say(f"canary fa_fwd_splitkv_paged H={H} H_kv={H_kv}")
+    op, lp = Padded((S, 3, H, 1, w.d), torch.float32, dev), Padded((S, 3, H, 1), torch.float32, dev)
     fa.fwd_splitkv_paged(q, kc, vc, bt, sl, S, o_part=op.view, lse_part=lp.view)
     check([op, lp], fa.fwd_splitkv_paged(q, kc, vc, bt, sl, S), "paged partials")
 

@@ -39,6 +39,8 @@ CASES = [  # B, H, H_kv, d, page_size, lengths, splits, dtype
     (1, 16, 2, 64, 256, (3000,), 7, F16),
     (2, 8, 1, 128, 32, (5, 17), 8, F16),                 # MQA; fewer keys than splits
     (2, 64, 8, 128, 16, (700, 1500), 5, BF16),           # 8 query heads per workgroup
+    (2, 8, 4, 128, 1, (300, 1201), 6, F16),              # 4 K/V heads per workgroup, 2 query heads each
+    (3, 16, 4, 128, 16, (0, 1, 999), 4, BF16),           # 4 K/V heads per workgroup; an empty sequence
 ]
 
 
@@ -62,10 +64,12 @@ def test_paged_decode(dev, oracle_lib, ci, case):
     parity.check(o.reshape(B, H, d), lse.reshape(B, H), ro, rl, dt, f"paged decode {case}")
 
 
-def test_paged_bad_entries(dev, oracle_lib):
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (16, 4)], ids=["kv2", "kv4"])
+def test_paged_bad_entries(dev, oracle_lib, H, H_kv):
     """A page entry outside [0, num_pages) drops its keys; a length beyond the
-    table leaves that sequence's partials unwritten."""
-    B, H, H_kv, d, ps, S = 3, 8, 2, 128, 16, 4
+    table leaves that sequence's partials unwritten (H_kv = 4: the kernel that
+    takes four K/V heads per workgroup)."""
+    B, d, ps, S = 3, 128, 16, 4
     lens = [100, 80, 50]
     w = BY_NAME["decode_paged"].with_(B=B, H=H, H_kv=H_kv, d=d, page_size=ps, seed=70)
     q, kc, vc, bt, sl = make_paged(w, seqlens=lens)
