@@ -106,14 +106,16 @@ __device__ __forceinline__ float dot2(u32 a, u32 b, float acc) {
 }
 
 // GP: query heads per workgroup (a divisor of the group size).  KV: dense
-// [B, H_kv, Nk, d] keys, the paged caches, or packed sequences.
-template <bool BF16, int D, int GP, int KV>
-__global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
+// [B, H_kv, Nk, d] keys, the paged caches, or packed sequences.  NWV wavefronts
+// share a (sequence, query heads, split); wave w takes the key groups w, w + NWV,
+// ... of the split.
+template <bool BF16, int D, int GP, int KV, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void decode_kernel(DecArgs a) {
     constexpr bool PAGED = KV == KV_PAGED;
     constexpr int CH = D / 8;          // lanes per key row
     constexpr int KPI = 64 / CH;       // key rows per wavefront load
     constexpr int U = GP >= 4 ? 4 : 8; // key groups in flight per step
-    constexpr int NP = 4 * KPI;        // partial states per workgroup and query head
+    constexpr int NP = NWV * KPI;      // partial states per workgroup and query head
     __shared__ float s_m[GP][NP], s_l[GP][NP];
     __shared__ __attribute__((aligned(16))) float s_o[GP][NP * D];
 
@@ -238,12 +240,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         const int wu = __builtin_amdgcn_readfirstlane(w);
         const int ksu = __builtin_amdgcn_readfirstlane(ks), keu = __builtin_amdgcn_readfirstlane(ke);
         const u32 lo = (u32)((r * a.H_kv * D + 8 * c) * 2);
-        for (int g0 = wu; g0 < ngroups; g0 += 4 * U) {
+        for (int g0 = wu; g0 < ngroups; g0 += NWV * U) {
             u32x4 kr[U], vr[U];
             bool ok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int kf = ksu + (g0 + 4 * u) * KPI;              // the group's first key
+                const int kf = ksu + (g0 + NWV * u) * KPI;              // the group's first key
                 const int pg = kf < keu ? __builtin_amdgcn_readfirstlane(bt[kf >> a.page_shift]) : -1;
                 const bool pok = (unsigned)pg < (unsigned)a.num_pages;
                 const int nrows = pok ? min(KPI, keu - kf) : 0;
@@ -261,15 +263,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         // page entries of the first step (paged)
         int pnext[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) pnext[u] = PAGED ? page_of(ks + (w + 4 * u) * KPI + r) : 0;
+        for (int u = 0; u < U; ++u) pnext[u] = PAGED ? page_of(ks + (w + NWV * u) * KPI + r) : 0;
 
-        for (int g0 = w; g0 < ngroups; g0 += 4 * U) {
+        for (int g0 = w; g0 < ngroups; g0 += NWV * U) {
             u32x4 kr[U], vr[U];
             int key[U];
             bool ok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                key[u] = ks + (g0 + 4 * u) * KPI + r;
+                key[u] = ks + (g0 + NWV * u) * KPI + r;
                 size_t row;
                 if constexpr (PAGED) {
                     // a page entry outside [0, num_pages) drops its keys
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
             }
             if constexpr (PAGED) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) pnext[u] = page_of(key[u] + 4 * U * KPI);   // next step's keys
+                for (int u = 0; u < U; ++u) pnext[u] = page_of(key[u] + NWV * U * KPI);   // next step's keys
             }
             consume(kr, vr, ok);
         }
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         for (int i = 0; i < 8; ++i) s_o[g][pidx * D + 8 * c + i] = acc[g][i];
     }
     __syncthreads();
-    for (int t = tid; t < GP * D; t += 256) {
+    for (int t = tid; t < GP * D; t += 64 * NWV) {
         const int g = t / D, col = t % D;
         float Ms = -INFINITY;
         for (int i = 0; i < NP; ++i) Ms = fmaxf(Ms, s_m[g][i]);
@@ -530,7 +532,14 @@ template <bool BF16, int D, int KV>
 hipError_t launch_dec(const DecArgs& a, int gp, int blocks, hipStream_t stream) {
     switch (gp) {
         case 8: hipLaunchKernelGGL((decode_kernel<BF16, D, 8, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
+        case 4:
+            // d = 128: eight wavefronts per (sequence, 4 query heads, split), as the
+            // packed layout takes (the two then give the same partials bit for bit)
+            if constexpr (D == 128 && KV == KV_DENSE) {
+                hipLaunchKernelGGL((decode_kernel<BF16, D, 4, KV, 8>), dim3(blocks), dim3(512), 0, stream, a);
+                break;
+            }
+            hipLaunchKernelGGL((decode_kernel<BF16, D, 4, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
         case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
         default: hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV>), dim3(blocks), dim3(256), 0, stream, a); break;
     }
@@ -596,7 +605,18 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
         return launch_paged_hg(a, p.bf16, (int)hb, stream);
     }
     if (p.block_table) return launch_dec_d<KV_PAGED>(a, p.d, p.bf16, gp, (int)blocks, stream);
-    if (p.varlen) return launch_dec_d<KV_PACKED>(a, p.d, p.bf16, gp, (int)blocks, stream);
+    if (p.varlen) {
+        // packed sequences differ in length and the longest splits set the time:
+        // eight wavefronts per workgroup stream a split twice as fast (decode_varlen
+        // 124.5 -> 118.5 us, sixteen measured 134 us; the dense grouped decode takes
+        // eight too, 192.7 -> 188.7 us)
+        if (p.d == 128 && gp == 4) {
+            if (p.bf16) hipLaunchKernelGGL((decode_kernel<true, 128, 4, KV_PACKED, 8>), dim3((int)blocks), dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((decode_kernel<false, 128, 4, KV_PACKED, 8>), dim3((int)blocks), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
+        return launch_dec_d<KV_PACKED>(a, p.d, p.bf16, gp, (int)blocks, stream);
+    }
     return launch_dec_d<KV_DENSE>(a, p.d, p.bf16, gp, (int)blocks, stream);
 }
 
