@@ -28,10 +28,15 @@
 // question on PagedAttention): keys live in pages of page_size rows
 // [num_pages, page_size, H_kv, d]; sequence b's logical page j sits in the
 // physical page block_table[b][j].  A key row stays 256 contiguous bytes (d =
-// 128), so every wavefront load still reads whole rows; each lane resolves its
-// own key's page, and the page entries of the next step are fetched one step
-// ahead so the indirection adds no latency.  Each sequence has its own length
-// and is split into num_splits equal chunks.
+// 128), so every wavefront load still reads whole rows.  Each sequence has its
+// own length and is split into num_splits equal chunks.  With 2 or 4 query heads
+// per K/V head and H_kv a multiple of 4, decode_paged_hg_kernel reads one key of
+// four adjacent K/V heads per wave load (their rows are contiguous in a page)
+// with one scalar page lookup per key; otherwise decode_kernel looks pages up
+// per wave load (scalar) or per lane.
+//
+// At d = 128 with 4 query heads per workgroup, contiguous and packed keys use
+// eight wavefronts per workgroup, which stream one split twice as fast.
 //
 // Packed sequences (the varlen interface with cumulative offsets instead of
 // padding, Ringi, "Lecture 25", section 7; split-KV for decode, LLM Infra Atlas,
