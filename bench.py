@@ -436,7 +436,7 @@ def main():
         gb = 2 * (2 * wg.B * wg.H * wg.d + 2 * wg.B * wg.H_kv * wg.Nk * wg.d) + 4 * wg.B * wg.H
         out["decode_gqa"], out["roofline_decode_gqa"] = decode_block(
             "decode_gqa", gb, gb - 2 * wg.B * wg.H * wg.d - 4 * wg.B * wg.H,
-            "decode_kernel<fp16, d=128, 4 query heads per workgroup>", "decode_gqa")
+            "decode_kernel<fp16, d=128, 4 query heads and 8 wavefronts per workgroup>", "decode_gqa")
         cfg["decode_gqa"] = {"B": wg.B, "H": wg.H, "H_kv": wg.H_kv, "Nq": wg.Nq, "Nk": wg.Nk, "d": wg.d,
                              "dtype": "fp16", "splits": wg.splits}
         if args.only == "decode_gqa":
@@ -449,7 +449,7 @@ def main():
         pgb = 2 * 2 * wpg.B * wpg.H * wpg.d + kv + 4 * wpg.B * wpg.H + 4 * pbt.numel()
         out["decode_paged"], out["roofline_decode_paged"] = decode_block(
             "decode_paged", pgb, pgb - 2 * wpg.B * wpg.H * wpg.d - 4 * wpg.B * wpg.H,
-            "decode_kernel<fp16, d=128, 4 query heads per workgroup, paged>", "decode_paged")
+            "decode_paged_hg_kernel<fp16, 4 K/V heads and 16 wavefronts per workgroup>", "decode_paged")
         cfg["decode_paged"] = {"B": wpg.B, "H": wpg.H, "H_kv": wpg.H_kv, "Nq": 1, "Nk": wpg.Nk, "d": wpg.d,
                                "dtype": "fp16", "splits": wpg.splits, "page_size": wpg.page_size}
         if args.only == "decode_paged":
@@ -462,7 +462,7 @@ def main():
         vgb = 2 * 2 * wdv.B * wdv.H * wdv.d + 2 * 2 * tk * wdv.H_kv * wdv.d + 4 * wdv.B * wdv.H + 4 * (wdv.B + 1)
         out["decode_varlen"], out["roofline_decode_varlen"] = decode_block(
             "decode_varlen", vgb, vgb - 2 * wdv.B * wdv.H * wdv.d - 4 * wdv.B * wdv.H,
-            "decode_kernel<fp16, d=128, 4 query heads per workgroup, packed>", "decode_varlen")
+            "decode_kernel<fp16, d=128, 4 query heads and 8 wavefronts per workgroup, packed>", "decode_varlen")
         cfg["decode_varlen"] = {"sequences": wdv.B, "keys": tk, "max_seqlen_k": max(wdv.seqlens), "H": wdv.H,
                                 "H_kv": wdv.H_kv, "Nq": 1, "d": wdv.d, "dtype": "fp16", "splits": wdv.splits}
         if args.only == "decode_varlen":
