@@ -110,6 +110,53 @@ __device__ __forceinline__ float dot2(u32 a, u32 b, float acc) {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
 }
 
+// One step of a decode wave: the scores of U key rows (this lane's 8 values of
+// each in kr) against GP queries (qp), the online-softmax update of the GP
+// states M, l, acc, and P V accumulation with the U value rows (vr).  A key that
+// does not exist (ok false) scores -inf; its K and V values are zeros.  CH lanes
+// hold one key row.
+template <bool BF16, int CH, int GP, int U>
+__device__ __forceinline__ void decode_step(const u32x4 (&qp)[GP], const u32x4* kr, const u32x4* vr, const bool* ok,
+                                            float c, float (&M)[GP], float (&l)[GP], float (&acc)[GP][8]) {
+    float s[GP][U];
+    float mx[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = dot2<BF16>(qp[g][i], kr[u][i], part);
+            s[g][u] = row_sum<CH>(part) * c;
+            if (!ok[u]) s[g][u] = -INFINITY;
+            mx[g] = fmaxf(mx[g], s[g][u]);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        const float Mn = fmaxf(M[g], mx[g]);
+        const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M[g] - Mn);
+        M[g] = Mn;
+        l[g] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float vf[8];
+        widen8<BF16>(vr[u], vf);
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            const float p = exp2_fast(s[g][u] - ((M[g] == -INFINITY) ? 0.f : M[g]));
+            l[g] += p;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(p, vf[i], acc[g][i]);
+        }
+    }
+}
+
 // GP: query heads per workgroup (a divisor of the group size).  KV: dense
 // [B, H_kv, Nk, d] keys, the paged caches, or packed sequences.  NWV wavefronts
 // share a (sequence, query heads, split); wave w takes the key groups w, w + NWV,
@@ -187,47 +234,8 @@ __global__ __launch_bounds__(64 * NWV) void decode_kernel(DecArgs a) {
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
     }
 
-    // One step's scores, online-softmax update and P V accumulation over the U
-    // key groups in registers; a key that does not exist (ok false) scores -inf
-    // and its K and V values are zeros.
     auto consume = [&](const u32x4* kr, const u32x4* vr, const bool* ok) {
-        float s[GP][U];
-        float mx[GP];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                float part = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) part = dot2<BF16>(qp[g][i], kr[u][i], part);
-                s[g][u] = row_sum<CH>(part) * a.c;
-                if (!ok[u]) s[g][u] = -INFINITY;
-                mx[g] = fmaxf(mx[g], s[g][u]);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const float Mn = fmaxf(M[g], mx[g]);
-            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M[g] - Mn);
-            M[g] = Mn;
-            l[g] *= alpha;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[8];
-            widen8<BF16>(vr[u], vf);
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                const float p = exp2_fast(s[g][u] - ((M[g] == -INFINITY) ? 0.f : M[g]));
-                l[g] += p;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(p, vf[i], acc[g][i]);
-            }
-        }
+        decode_step<BF16, CH, GP, U>(qp, kr, vr, ok, a.c, M, l, acc);
     };
 
     // Paged keys whose groups never straddle a page (the split starts at a
@@ -396,43 +404,7 @@ __global__ __launch_bounds__(1024) void decode_paged_hg_kernel(DecArgs a) {
             kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lo, 0, 0));
             vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo, 0, 0));
         }
-        float s[GP][U];
-        float mx[GP];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                float part = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) part = dot2<BF16>(qp[g][i], kr[u][i], part);
-                s[g][u] = row_sum<CH>(part) * a.c;
-                if (!ok[u]) s[g][u] = -INFINITY;
-                mx[g] = fmaxf(mx[g], s[g][u]);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const float Mn = fmaxf(M[g], mx[g]);
-            const float alpha = (Mn == -INFINITY) ? 1.f : exp2_fast(M[g] - Mn);
-            M[g] = Mn;
-            l[g] *= alpha;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[8];
-            widen8<BF16>(vr[u], vf);
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                const float p = exp2_fast(s[g][u] - ((M[g] == -INFINITY) ? 0.f : M[g]));
-                l[g] += p;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(p, vf[i], acc[g][i]);
-            }
-        }
+        decode_step<BF16, CH, GP, U>(qp, kr, vr, ok, a.c, M, l, acc);
     }
 
 #pragma unroll
