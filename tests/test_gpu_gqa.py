@@ -59,7 +59,8 @@ def test_fwd_gqa(dev, oracle_lib, case):
 DEC = [  # B, H, H_kv, Nk, d, splits, dtype
     (2, 8, 8, 1000, 128, 4, F16),      # 1 query head per workgroup
     (2, 8, 4, 777, 128, 3, BF16),      # 2
-    (1, 8, 2, 3000, 128, 8, F16),      # 4
+    (1, 8, 2, 3000, 128, 8, F16),      # 4 (eight wavefronts per workgroup at d = 128)
+    (2, 16, 4, 1531, 128, 6, BF16),    # 4, bf16, a ragged split tail
     (1, 16, 2, 2049, 64, 5, BF16),     # 8
     (1, 32, 2, 513, 128, 2, F16),      # group of 16: two workgroups of 8
     (2, 6, 2, 100, 64, 7, F16),        # group of 3: one query head per workgroup
