@@ -239,21 +239,45 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW], i
 // the dispatcher's own round-robin order instead: packed sequences differ in
 // work by orders of magnitude, and contiguous ranges would put a long sequence's
 // heads on one XCD.
+//
+// With packed sequences (cu, the B + 1 offsets of the lengths that set the work)
+// the heads of the longest sequence come first, then the next longest: the
+// longest items start first and the short ones fill the end of the grid.  Every
+// wavefront ranks the B <= 64 lengths itself (one lane per sequence; equal
+// lengths keep their index order, so the ranks are a permutation and every item
+// runs exactly once); with more sequences the index order is kept.
+__device__ __forceinline__ int seq_at_rank(const int* cu, int B, int p) {
+    const int lane = threadIdx.x & 63;
+    const int len = lane < B ? cu[lane + 1] - cu[lane] : 0;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+        const int lj = __builtin_amdgcn_readlane(len, j);
+        rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long m = __ballot(lane < B && rank == p);
+    return m ? (int)__builtin_ctzll(m) : p;
+}
+
 template <bool PAIR, bool XCD = true, class F>
-__device__ __forceinline__ void for_items(int per_head, int BH, F&& item) {
+__device__ __forceinline__ void for_items(int per_head, int BH, F&& item, const int* cu = nullptr, int heads = 1) {
     const int total = gridDim.x;
     int L = blockIdx.x;
     if (XCD && (total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    auto order = [&](int bh) {
+        const int B = BH / heads;
+        if (cu == nullptr || B > 64) return bh;
+        return seq_at_rank(cu, B, bh / heads) * heads + bh % heads;
+    };
     if (PAIR && per_head >= 2) {
         const int npairs = (per_head + 1) >> 1;
-        const int t = L % npairs, bh = L / npairs;
+        const int t = L % npairs, bh = order(L / npairs);
         item(t, bh);
         if (t != per_head - 1 - t) {
             __syncthreads();        // the next item refills the LDS stages
             item(per_head - 1 - t, bh);
         }
     } else {
-        item(L % per_head, (L / per_head) % BH);
+        item(L % per_head, order((L / per_head) % BH));
     }
 }
 
@@ -468,7 +492,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdArgs a) {
         store_rows_staged<BF16, D>(dqacc, a.scale, (w < 4 ? stage0 : stage1) + (w & 3) * (32 * ROWB), a.dq + sg.q,
                                    sg.sq, qw, Nq, lane);
     };
-    for_items<CAUSAL, !VARLEN>(a.n_qtiles, a.BH, run_item);
+    for_items<CAUSAL, !VARLEN>(a.n_qtiles, a.BH, run_item, VARLEN ? a.cu_q : nullptr, a.H);
 }
 
 // ---- dK, dV -------------------------------------------------------------------
@@ -731,7 +755,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         store_rows_staged<BF16, D>(dkacc, a.scale, stage0 + w * (32 * ROWB), a.dk + sg.k, sg.sk, kw, Nk, lane);
         store_rows_staged<BF16, D>(dvacc, 1.f, stage1 + w * (32 * ROWB), a.dv + sg.k, sg.sk, kw, Nk, lane);
     };
-    for_items<CAUSAL, !VARLEN>(a.n_ktiles, a.BH / a.group, run_item);   // over the K/V heads
+    // over the K/V heads; packed sequences longest first
+    for_items<CAUSAL, !VARLEN>(a.n_ktiles, a.BH / a.group, run_item, VARLEN ? a.cu_k : nullptr, a.H_kv);
 }
 
 // 8-wavefront dQ workgroups for dense d = 128 over long key ranges
