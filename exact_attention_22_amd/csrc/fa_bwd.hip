@@ -243,21 +243,8 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, u32 (&voff)[NPW], i
 // With packed sequences (cu, the B + 1 offsets of the lengths that set the work)
 // the heads of the longest sequence come first, then the next longest: the
 // longest items start first and the short ones fill the end of the grid.  Every
-// wavefront ranks the B <= 64 lengths itself (one lane per sequence; equal
-// lengths keep their index order, so the ranks are a permutation and every item
-// runs exactly once); with more sequences the index order is kept.
-__device__ __forceinline__ int seq_at_rank(const int* cu, int B, int p) {
-    const int lane = threadIdx.x & 63;
-    const int len = lane < B ? cu[lane + 1] - cu[lane] : 0;
-    int rank = 0;
-    for (int j = 0; j < B; ++j) {
-        const int lj = __builtin_amdgcn_readlane(len, j);
-        rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
-    }
-    const unsigned long long m = __ballot(lane < B && rank == p);
-    return m ? (int)__builtin_ctzll(m) : p;
-}
-
+// wavefront ranks the B <= 64 lengths itself (seq_at_rank); with more sequences
+// the index order is kept.
 template <bool PAIR, bool XCD = true, class F>
 __device__ __forceinline__ void for_items(int per_head, int BH, F&& item, const int* cu = nullptr, int heads = 1) {
     const int total = gridDim.x;

@@ -1,7 +1,8 @@
 // fa_device.h -- gfx950 (CDNA4) building blocks shared by the attention kernels.
 //
 // Only device code lives here: MFMA wrappers, 16-bit packing, LDS transpose
-// reads, the cross-half lane exchange, and the LDS swizzle.
+// reads, the cross-half lane exchange, the LDS swizzle, buffer loads into LDS,
+// and the length ranking of packed sequences.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -117,6 +118,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds, u32 voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds,
                                              16, voff, 0, 0, 0);
+}
+
+// The packed sequence of rank p when the B <= 64 sequences are ordered by
+// length cu[b+1] - cu[b], longest first (equal lengths in index order, so the
+// ranks are a permutation of 0..B-1).  Every lane of the wavefront must call it;
+// lane b takes sequence b and counts the sequences ranked before it.
+__device__ __forceinline__ int seq_at_rank(const int* cu, int B, int p) {
+    const int lane = threadIdx.x & 63;
+    const int len = lane < B ? cu[lane + 1] - cu[lane] : 0;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+        const int lj = __builtin_amdgcn_readlane(len, j);
+        rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long m = __ballot(lane < B && rank == p);
+    return m ? (int)__builtin_ctzll(m) : p;
 }
 
 }  // namespace fa

@@ -494,7 +494,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
         const int per_group = a.group * ((a.n_qtiles + 1) >> 1);
         const int j = blockIdx.x >> 3, gi = j / per_group, r = j - gi * per_group;
         const int grp = gi * 8 + (blockIdx.x & 7);
-        const int b = grp / a.H_kv, hk = grp - b * a.H_kv;
+        const int hk = grp % a.H_kv;
+        // sequences longest first (B <= 64; otherwise in index order): the longest
+        // items start first and short ones fill the end of the grid
+        const int b = a.B <= 64 ? seq_at_rank(a.cu_q, a.B, grp / a.H_kv) : grp / a.H_kv;
         const int t = r / a.group, bh = b * a.H + hk * a.group + r % a.group;
         const int len = a.cu_q[b + 1] - a.cu_q[b];     // run_item checks the offsets themselves
         const int nb = (len > 0 && len <= a.max_q) ? (len + BR - 1) / BR : 0;
