@@ -447,8 +447,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // One wavefront per output row.  Lane l reads the LSE of split l (64 splits per
-// pass), so the row's weights come from one round of loads instead of S
-// dependent ones; the weighted partial rows are then summed in split order.
+// pass), and the first 16 partial rows are requested in the same round of loads,
+// before the row maximum is known, so a decode with up to 16 splits waits for
+// memory once; the weighted rows are then summed in split order (16 rows' loads
+// in flight per later round).
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ op, const float* __restrict__ lp,
                                                       uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -456,31 +458,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= R) return;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < S; s0 += 64)
+    constexpr int nd = D / 64;   // values per lane (1 or 2)
+    constexpr int SB = 16;       // partial rows per round of loads
+    auto load_rows = [&](float (&x)[SB][nd], int j0, int ns) {
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int j = min(j0 + u, ns - 1);     // in bounds; rows past ns get weight 0
+            const float* src = op + ((size_t)j * R + row) * D;
+#pragma unroll
+            for (int c = 0; c < nd; ++c) x[u][c] = src[lane + 64 * c];
+        }
+    };
+    const float ls_first = lane < S ? lp[(size_t)lane * R + row] : -INFINITY;
+    float x[SB][nd];
+    load_rows(x, 0, S);
+    float M = ls_first;
+    for (int s0 = 64; s0 < S; s0 += 64)
         if (s0 + lane < S) M = fmaxf(M, lp[(size_t)(s0 + lane) * R + row]);
     M = wave_max(M);
-    constexpr int nd = D / 64;   // values per lane (1 or 2)
     float num[2] = {0.f, 0.f};
     float den = 0.f;
     if (M != -INFINITY) {
         for (int s0 = 0; s0 < S; s0 += 64) {
-            const float ls = (s0 + lane < S) ? lp[(size_t)(s0 + lane) * R + row] : -INFINITY;
+            const float ls = s0 == 0 ? ls_first : ((s0 + lane < S) ? lp[(size_t)(s0 + lane) * R + row] : -INFINITY);
             const float wl = (ls == -INFINITY) ? 0.f : exp2_fast((ls - M) * kLog2e);
             den += wl;
             const int ns = min(64, S - s0);
-            // eight splits per round so their loads are in flight together
-            for (int j0 = 0; j0 < ns; j0 += 8) {
-                float x[8][nd];
+            for (int j0 = 0; j0 < ns; j0 += SB) {
+                if (s0 + j0 > 0) load_rows(x, s0 + j0, s0 + ns);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = min(j0 + u, ns - 1);
-                    const float* src = op + ((size_t)(s0 + j) * R + row) * D;
-#pragma unroll
-                    for (int c = 0; c < nd; ++c) x[u][c] = src[lane + 64 * c];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < SB; ++u) {
                     const float wj = (j0 + u < ns) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0 + u))
                                                    : 0.f;
 #pragma unroll
