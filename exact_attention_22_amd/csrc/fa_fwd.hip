@@ -54,8 +54,9 @@
 //     (scheduling groups), so a wavefront's vector work runs while its own
 //     products occupy the matrix core.
 //   * A workgroup is 4 wavefronts (128 query rows, two workgroups per CU) or,
-//     over long key ranges, 8 (256 rows, one per CU), which loads each K/V tile
-//     into LDS once for twice the query rows.
+//     over long key ranges at d = 128 and over full grids at d = 64 without the
+//     mask, 8 (256 rows, one per CU), which loads each K/V tile into LDS once for
+//     twice the query rows.
 //   * Workgroups are mapped so that consecutive tiles of one head share an XCD
 //     (and its L2).  Causal [B, H, N, d]: one workgroup runs query tiles
 //     n_qtiles-1-t and t, which together see a fixed number of key tiles, so
@@ -541,7 +542,7 @@ hipError_t launch_t(const FwdArgs& a, int blocks, hipStream_t stream) {
 }
 
 // mode: 0 plain [B,H,N,d], 1 split-KV partials, 2 packed variable-length; wide:
-// eight wavefronts per workgroup (plain mode only)
+// eight wavefronts per workgroup (plain mode only; with the causal mask, d = 128 only)
 template <bool BF16, int D>
 hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, int mode, bool wide, hipStream_t s) {
     if (causal) {
@@ -553,8 +554,7 @@ hipError_t dispatch_cs(const FwdArgs& a, int blocks, bool causal, int mode, bool
     }
     if (mode == 1) return launch_t<BF16, D, false, true, false, 4>(a, blocks, s);
     if (mode == 2) return launch_t<BF16, D, false, false, true, 4>(a, blocks, s);
-    if constexpr (D == 128)
-        if (wide) return launch_t<BF16, D, false, false, false, 8>(a, blocks, s);
+    if (wide) return launch_t<BF16, D, false, false, false, 8>(a, blocks, s);
     return launch_t<BF16, D, false, false, false, 4>(a, blocks, s);
 }
 
@@ -577,10 +577,16 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     const bool split = p.num_splits > 0;
     const int mode = p.varlen ? 2 : (split ? 1 : 0);
     // Each workgroup loads every K/V tile it attends to once for its query rows,
-    // so over long key ranges 256 query rows per workgroup (eight wavefronts, one
-    // workgroup per CU) halve the K/V traffic into LDS; on shorter ones the
-    // finer grid of 128-row workgroups (two per CU) balances better.
-    const bool wide = mode == 0 && p.d == 128 && p.Nk >= 4096;
+    // so 256 query rows per workgroup (eight wavefronts, one workgroup per CU)
+    // halve the K/V traffic into LDS, with half as many workgroups.  Measured over
+    // B, H, N, d and the mask: at d = 128 they win from 2048 keys on as long as the
+    // grid keeps at least 128 workgroups; at d = 64 without the mask whenever the
+    // grid fills the 256 CUs; elsewhere the finer grid of 128-row workgroups (two
+    // per CU) balances better.
+    const int64_t nq_wide = (p.Nq + 255) / 256;
+    const int64_t wide_blocks = (p.causal ? (nq_wide + 1) / 2 : nq_wide) * (int64_t)p.B * p.H;
+    const bool wide = mode == 0 && (p.d == 128 ? (p.Nk >= 2048 && wide_blocks >= 128)
+                                               : (!p.causal && wide_blocks >= 256));
     const int BR = wide ? 256 : 128;
     a.n_qtiles = (p.Nq + BR - 1) / BR;        // varlen: Nq is the longest query sequence
     const int S = split ? p.num_splits : 1;
@@ -601,8 +607,8 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     if (p.d == 128)
         return p.bf16 ? dispatch_cs<true, 128>(a, (int)blocks, p.causal, mode, wide, stream)
                       : dispatch_cs<false, 128>(a, (int)blocks, p.causal, mode, wide, stream);
-    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, mode, false, stream)
-                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, mode, false, stream);
+    return p.bf16 ? dispatch_cs<true, 64>(a, (int)blocks, p.causal, mode, wide, stream)
+                  : dispatch_cs<false, 64>(a, (int)blocks, p.causal, mode, wide, stream);
 }
 
 }  // namespace fa

@@ -64,6 +64,37 @@ def test_fwd_small(dev, oracle_lib, case):
     parity.check(o, lse, ro, rl, dt, f"fwd {case}")
 
 
+# Shapes that take 256-row workgroups of eight wavefronts: at d = 128 from 2048
+# keys on with at least 128 such workgroups, at d = 64 without the mask with at
+# least 256 of them; tails ragged against both 256 rows and 64 keys.
+WIDE = [  # B, H, H_kv, Nq, Nk, d, causal, dtype
+    (1, 32, 32, 2100, 2100, 128, True, F16),
+    (1, 32, 32, 1900, 2300, 128, True, BF16),    # Nq < Nk: bottom-right diagonal
+    (1, 16, 16, 2200, 2049, 128, False, F16),
+    (2, 16, 16, 2000, 2000, 64, False, F16),
+    (1, 32, 32, 2049, 777, 64, False, BF16),
+    (1, 32, 8, 2100, 2100, 64, False, F16),      # grouped K/V heads
+    (1, 32, 8, 2100, 2100, 128, True, BF16),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}-{str(c[7])[-4:]}")
+def test_fwd_wide(dev, oracle_lib, case):
+    B, H, Hkv, Nq, Nk, d, causal, dt = case
+    q, k, v = rnd((B, H, Nq, d), dt, 11), rnd((B, Hkv, Nk, d), dt, 12), rnd((B, Hkv, Nk, d), dt, 13)
+    say(f"fa_fwd{'_gqa' if Hkv != H else ''} 8-wavefront workgroups {case}")
+    if Hkv == H:
+        o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    else:
+        o, lse = fa.fwd_gqa(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    if Hkv == H:
+        ro, rl = oracle_lib.attention(q, k, v, causal, 1 / math.sqrt(d))
+    else:
+        ro, rl = oracle_lib.attention_gqa(q, k, v, causal, 1 / math.sqrt(d))
+    parity.check(o, lse, ro, rl, dt, f"wide {case}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
 def test_fwd_scales(dev, oracle_lib, scale):
     B, H, N, d = 1, 2, 130, 64
