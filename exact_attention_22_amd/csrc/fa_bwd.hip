@@ -746,8 +746,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for_items<CAUSAL, !VARLEN>(a.n_ktiles, a.BH / a.group, run_item, VARLEN ? a.cu_k : nullptr, a.H_kv);
 }
 
-// 8-wavefront dQ workgroups for dense d = 128 over long key ranges
-inline bool dq_wide(bool varlen, int d, int Nk) { return !varlen && d == 128 && Nk >= 4096; }
+// 8-wavefront dQ workgroups for dense d = 128 where they beat 4 (wide_rows; the
+// dQ walk wins from 1024 keys on)
+inline bool dq_wide(bool varlen, int d, int Nq, int Nk, int64_t bh, bool causal) {
+    return !varlen && d == 128 && wide_rows(wide_blocks(Nq, bh, causal), Nk, 1024);
+}
 
 template <bool BF16, int D, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t s) {
@@ -755,7 +758,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool causal, int64_t rows, hipStream_t
     hipLaunchKernelGGL((bwd_delta_kernel<BF16, D, VARLEN>), dim3((int)dblocks), dim3(256), 0, s, a, rows);
     const int kv_blocks = (int)item_blocks(causal, a.n_ktiles, a.BH / a.group);
     const int q_blocks = (int)item_blocks(causal, a.n_qtiles, a.BH);
-    const bool wide = dq_wide(VARLEN, D, a.Nk);
+    const bool wide = dq_wide(VARLEN, D, a.Nq, a.Nk, a.BH, causal);
     if (causal) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, true, VARLEN>), dim3(kv_blocks), dim3(256), 0, s, a);
         if constexpr (D == 128 && !VARLEN)
@@ -814,7 +817,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     a.Nk = p.Nk;
     a.c = p.scale * kLog2e;
     a.scale = p.scale;
-    const int bq = dq_wide(varlen, p.d, p.Nk) ? 2 * BQ : BQ;
+    const int bq = dq_wide(varlen, p.d, p.Nq, p.Nk, (int64_t)p.B * p.H, p.causal) ? 2 * BQ : BQ;
     a.n_qtiles = (p.Nq + bq - 1) / bq;
     a.n_ktiles = (p.Nk + CK - 1) / CK;
     if ((int64_t)a.n_qtiles * a.BH > 0x7fffffff || (int64_t)a.n_ktiles * a.BH > 0x7fffffff ||

@@ -414,8 +414,8 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream) {
     a.Nq = p.Nq;
     a.Nk = p.Nk;
     a.BH = p.B * p.H;
-    // 8 wavefronts (256 query rows per workgroup) over long key ranges
-    const bool wide = p.Nk >= 4096;
+    // 8 wavefronts (256 query rows per workgroup) where they beat 4 (wide_rows)
+    const bool wide = wide_rows(wide_blocks(p.Nq, (int64_t)p.B * p.H, p.causal), p.Nk, 2048);
     const int br = wide ? 256 : 128;
     a.n_qtiles = (p.Nq + br - 1) / br;
     a.n_qblk = (p.Nq + F8_QB - 1) / F8_QB;

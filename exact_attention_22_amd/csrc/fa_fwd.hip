@@ -578,15 +578,12 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     const int mode = p.varlen ? 2 : (split ? 1 : 0);
     // Each workgroup loads every K/V tile it attends to once for its query rows,
     // so 256 query rows per workgroup (eight wavefronts, one workgroup per CU)
-    // halve the K/V traffic into LDS, with half as many workgroups.  Measured over
-    // B, H, N, d and the mask: at d = 128 they win from 2048 keys on as long as the
-    // grid keeps at least 128 workgroups; at d = 64 without the mask whenever the
-    // grid fills the 256 CUs; elsewhere the finer grid of 128-row workgroups (two
-    // per CU) balances better.
-    const int64_t nq_wide = (p.Nq + 255) / 256;
-    const int64_t wide_blocks = (p.causal ? (nq_wide + 1) / 2 : nq_wide) * (int64_t)p.B * p.H;
-    const bool wide = mode == 0 && (p.d == 128 ? (p.Nk >= 2048 && wide_blocks >= 128)
-                                               : (!p.causal && wide_blocks >= 256));
+    // halve the K/V traffic into LDS, with half as many workgroups (wide_rows).  At
+    // d = 64, where the softmax bounds the kernel, the wider form wins 3-6% without
+    // the mask whenever the grid fills the 256 CUs; with the mask it gained at most
+    // 3% and lost up to a third on smaller grids, so there it is not used.
+    const int64_t wb = wide_blocks(p.Nq, (int64_t)p.B * p.H, p.causal);
+    const bool wide = mode == 0 && (p.d == 128 ? wide_rows(wb, p.Nk, 2048) : (!p.causal && wb >= 256));
     const int BR = wide ? 256 : 128;
     a.n_qtiles = (p.Nq + BR - 1) / BR;        // varlen: Nq is the longest query sequence
     const int S = split ? p.num_splits : 1;

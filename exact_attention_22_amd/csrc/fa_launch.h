@@ -87,6 +87,23 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                           int64_t rows, int d, int num_splits, bool bf16, hipStream_t stream);
 
+// Workgroups of 256 query rows (eight wavefronts, one per CU) against 128 rows
+// (four, two per CU) for a walk over nk keys, given how many 256-row workgroups
+// the launch would make: the wider ones load each tile once for twice the rows
+// but leave the grid half as fine.  Timed over B, H and N (256 to 16384) on the
+// forward, the FP8 forward and the dQ kernel, the wider ones win from min_keys
+// keys on when the grid keeps 256 of them, and from 4096 keys on with 128.
+inline bool wide_rows(int64_t wide_blocks, int nk, int min_keys) {
+    return (nk >= min_keys && wide_blocks >= 256) || (nk >= 4096 && wide_blocks >= 128);
+}
+
+// 256-row workgroups a launch over nq query rows of bh heads makes (causal:
+// query tiles t and n-1-t share a workgroup).
+inline int64_t wide_blocks(int nq, int64_t bh, bool causal) {
+    const int64_t n = (nq + 255) / 256;
+    return (causal ? (n + 1) / 2 : n) * bh;
+}
+
 // Keys per split chunk: ceil(Nk / num_splits).
 inline int split_chunk(int Nk, int num_splits) { return (Nk + num_splits - 1) / num_splits; }
 

@@ -80,6 +80,31 @@ def test_bwd_scales(dev, oracle_lib, scale):
         parity.check_grads((dq, dk, dv), (rq, rk, rv), F16, f"bwd scale {scale} causal {causal}")
 
 
+WIDE_DQ = [  # B, H, N, causal, dtype: dQ workgroups of 256 rows (1024 keys or more, 256 such workgroups)
+    (2, 32, 1100, False, BF16),
+    (4, 32, 1500, True, F16),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_DQ, ids=lambda c: "x".join(map(str, c[:3])) + f"-c{int(c[3])}-{('bf16' if c[4] == BF16 else 'f16')}")
+def test_bwd_wide_dq_sampled(dev, oracle_lib, case):
+    """Eight-wavefront dQ workgroups with ragged tails: the first and last rows of
+    every head and 128 seeded random query and key rows against the oracle."""
+    B, H, N, causal, dt = case
+    d = 128
+    q, k, v, g = (rnd((B, H, N, d), dt, s) for s in (21, 22, 23, 24))
+    say(f"fa_bwd eight-wavefront dQ workgroups {case}")
+    dq, dk, dv = run(dev, q, k, v, g, causal)
+    rng = np.random.default_rng(N)
+    heads = np.arange(B * H)
+    qr = np.unique(np.concatenate([heads * N, heads * N + N - 1, rng.integers(0, B * H * N, 128)]))
+    kr = np.unique(np.concatenate([heads * N, heads * N + N - 1, rng.integers(0, B * H * N, 128)]))
+    rq, rk, rv = oracle_lib.attention_bwd(q, k, v, g, causal, 1 / math.sqrt(d), q_rows=qr, k_rows=kr)
+    qi, ki = torch.from_numpy(qr).to(dev), torch.from_numpy(kr).to(dev)
+    parity.check_grads((dq.reshape(-1, d)[qi], dk.reshape(-1, d)[ki], dv.reshape(-1, d)[ki]),
+                       (rq, rk, rv), dt, f"bwd wide dQ {case} sampled")
+
+
 def test_bwd_workload(dev, oracle_lib):
     """causal_d128 (B=4 H=16 N=2048 d=128 fp16 causal) at full size, sampled rows of two heads."""
     w = BY_NAME["causal_d128"]

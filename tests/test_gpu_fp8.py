@@ -176,6 +176,40 @@ def test_fwd_fp8_random(dev, case):
     check_lse(lse, rl, f"random {case}")
 
 
+WIDE = [  # B, H, H_kv, N, causal: 256-row workgroups (2048 keys or more, 256 such workgroups)
+    (4, 16, 16, 2100, True),
+    (2, 32, 8, 2100, False),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}")
+def test_fwd_fp8_wide_sampled(dev, case):
+    """Eight-wavefront workgroups with ragged tails (2100 rows against 256-row
+    workgroups and 128-key tiles): the first, second and last rows of every head
+    and eight seeded random rows per head against the oracle."""
+    B, H, H_kv, N, causal = case
+    d = 128
+    g = torch.Generator().manual_seed(N + H)
+    q, k, v = (torch.randn(shape, generator=g).bfloat16() for shape in ((B, H, N, d), (B, H_kv, N, d), (B, H_kv, N, d)))
+    q8, qd = ofp8.quantize_blocks(q.reshape(B * H, N, d), 128)
+    k8, kd = ofp8.quantize_blocks(k.reshape(B * H_kv, N, d), 128)
+    v8, vd = ofp8.quantize_blocks(v.reshape(B * H_kv, N, d), N)
+    q8, qd = q8.reshape(B, H, N, d), qd.reshape(B, H, -1)
+    k8, kd = k8.reshape(B, H_kv, N, d), kd.reshape(B, H_kv, -1)
+    v8, vd = v8.reshape(B, H_kv, N, d), vd.reshape(B, H_kv)
+    scale = 1 / math.sqrt(d)
+    say(f"fa_fwd_fp8 eight-wavefront workgroups {case}")
+    o, lse = run_fp8(dev, q8, k8, v8, qd, kd, vd, causal, scale)
+    rng = np.random.default_rng(N)
+    heads = np.arange(B * H)
+    rows = np.unique(np.concatenate([heads * N, heads * N + 1, heads * N + N - 1,
+                                     np.repeat(heads, 8) * N + rng.integers(0, N, 8 * B * H)]))
+    ro, rl, A, U, R = ofp8.attention_fp8(q8, k8, v8, qd, kd, vd, causal, scale, rows=rows, spread=True)
+    idx = torch.from_numpy(rows).to(dev)
+    fp8_check.check(o.reshape(-1, d)[idx].double().cpu().numpy(), ro, A, U, R, f"wide {case}")
+    check_lse(lse.reshape(-1)[idx], rl, f"wide {case}")
+
+
 def test_fwd_fp8_long_causal_sampled(dev):
     """long_causal's shapes (B=1 H=32 N=8192 d=128 causal) quantized on the CPU
     by the oracle's quantizer; the first, second and last rows of every head and
