@@ -307,6 +307,10 @@ template <bool BF16, int D>
 __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float mul, unsigned char* reg,
                                                   uint16_t* dst, int row_stride, int row0, int n, int lane) {
     constexpr int ROWB = D * 2, CH = ROWB / 16, RPI = 1024 / ROWB;
+    // the lane's LDS addresses are formed here, after the walk: computed at the
+    // kernel's start (the compiler's choice otherwise) they would stay live across
+    // the whole walk and spill to scratch
+    asm volatile("" : "+v"(lane));
     const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
