@@ -135,20 +135,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(F8Args a) {
         if (CAUSAL) hi = min(hi, min(Nq, q0 + BR) + off);
         const int n_tiles = hi > 0 ? (hi + F8_BC - 1) / F8_BC : 0;
 
-        // Q: bytes 64ks + 32h .. +31 of this lane's row, for ks = 0, 1
-        i32x8 qf[2];
+        // Q: bytes 64ks + 32h .. +31 of this lane's row, for ks = 0, 1.  All four
+        // loads go out before any is used (rows past Nq read the last row and are
+        // zeroed, and the sign flipped, after the first tile's loads are issued).
+        u32x4 qx[4];
+        {
+            const u32x4* src = (const u32x4*)(qg + (size_t)min(qi, Nq - 1) * F8_D + 32 * h);
     #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (qi < Nq) {
-                const u32x4* src = (const u32x4*)(qg + (size_t)qi * F8_D + 64 * ks + 32 * h);
-                const u32x4 x0 = src[0], x1 = src[1];
-                qf[ks] = i32x8{(int)(x0[0] ^ a.qsign), (int)(x0[1] ^ a.qsign), (int)(x0[2] ^ a.qsign),
-                               (int)(x0[3] ^ a.qsign), (int)(x1[0] ^ a.qsign), (int)(x1[1] ^ a.qsign),
-                               (int)(x1[2] ^ a.qsign), (int)(x1[3] ^ a.qsign)};
-            } else {
-                qf[ks] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int ks = 0; ks < 2; ++ks) {
+                qx[2 * ks] = src[4 * ks];
+                qx[2 * ks + 1] = src[4 * ks + 1];
             }
         }
+        i32x8 qf[2];
 
         // LDS-direct loads: lane i of a 1 KiB load lands at byte 16 i; it fetches the
         // global chunk that the swizzled layout keeps there
@@ -283,6 +282,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(F8Args a) {
         }
         const int qmax_w = min(qw + 31, Nq - 1);
         if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
+        {
+            const u32 sg = qi < Nq ? a.qsign : 0u;
+            const u32 keep = qi < Nq ? ~0u : 0u;
+    #pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 x0 = qx[2 * ks], x1 = qx[2 * ks + 1];
+                qf[ks] = i32x8{(int)((x0[0] ^ sg) & keep), (int)((x0[1] ^ sg) & keep), (int)((x0[2] ^ sg) & keep),
+                               (int)((x0[3] ^ sg) & keep), (int)((x1[0] ^ sg) & keep), (int)((x1[1] ^ sg) & keep),
+                               (int)((x1[2] ^ sg) & keep), (int)((x1[3] ^ sg) & keep)};
+            }
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         // the masked tiles, then the clean ones, each two per trip so that every step

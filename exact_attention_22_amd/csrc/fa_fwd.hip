@@ -183,15 +183,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
         const int n_tiles = hi > ks ? (hi - ks + BC - 1) / BC : 0;
 
         // ---- Q fragments, resident for the whole key loop ----------------------
+        // Every load is issued before any is used (rows past Nq read the last row
+        // and are zeroed afterwards), so the item waits for memory once; a load
+        // inside the row check made each one wait for the previous.
         u32x4 qf[NS];
+        {
+            const uint16_t* qrow = qg + (size_t)min(qi, Nq - 1) * q_rs + 8 * h;
     #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if (qi < Nq) {
-                qf[s] = *(const u32x4*)(qg + (size_t)qi * q_rs + 16 * s + 8 * h);
-                qf[s] ^= a.qsign;
-            } else {
-                qf[s] = u32x4{0, 0, 0, 0};
-            }
+            for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qrow + 16 * s);
         }
 
         // ---- K/V tiles: buffer loads straight into LDS ---------------------------
@@ -390,6 +389,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdArgs a) {
         }
         const int qmax_w = min(qw + 31, Nq - 1);
         if (n_tiles > 0) load_tile(n_tiles - 1, stage0);
+        // the Q sign flip (and the zero rows) only now, so that the Q loads and the
+        // first tile's loads are in flight together
+        const bool qin = qi < Nq;
+    #pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = qin ? (qf[s] ^ a.qsign) : u32x4{0, 0, 0, 0};
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         // masked tiles: per-wave visibility checks, two per trip so that each step
