@@ -514,6 +514,13 @@ __device__ __forceinline__ void dkdv_probs(const f32x16& s, const f32x16& dp, co
     }
 }
 
+// Empty asm statements that take a value as an operand: the value's computation
+// is then ordered before the statement.  Scheduling fences order memory operations
+// only; without these, pure arithmetic (matrix products included) drifts past a
+// fence towards its first use.  The matrix accumulators live in the AGPR file.
+#define FA_PIN_A(x) asm volatile("" : "+a"(x))
+#define FA_PIN_V(x) asm volatile("" : "+v"(x))
+
 // Four of those rows (register 8p + e0 .. 8p + e0 + 3, e0 in {0, 4}): the same
 // values as dkdv_probs, written into words e0/2, e0/2 + 1 of pb[p] and sb[p].
 template <bool BF16, bool MASK>
@@ -526,10 +533,16 @@ __device__ __forceinline__ void dkdv_probs4(const f32x16& s, const f32x16& dp, c
         if (MASK) pr[e] = (16 * p + e0 + e < lim) ? 0.f : pr[e];
         ds[e] = pr[e] * (dp[8 * p + e0 + e] - d4[e]);
     }
-    pbp[e0 / 2] = pack2<BF16>(pr[0], pr[1]);
-    pbp[e0 / 2 + 1] = pack2<BF16>(pr[2], pr[3]);
-    sbp[e0 / 2] = pack2<BF16>(ds[0], ds[1]);
-    sbp[e0 / 2 + 1] = pack2<BF16>(ds[2], ds[3]);
+    u32 w0 = pack2<BF16>(pr[0], pr[1]), w1 = pack2<BF16>(pr[2], pr[3]);
+    u32 w2 = pack2<BF16>(ds[0], ds[1]), w3 = pack2<BF16>(ds[2], ds[3]);
+    FA_PIN_V(w0);
+    FA_PIN_V(w1);
+    FA_PIN_V(w2);
+    FA_PIN_V(w3);
+    pbp[e0 / 2] = w0;
+    pbp[e0 / 2 + 1] = w1;
+    sbp[e0 / 2] = w2;
+    sbp[e0 / 2 + 1] = w3;
 }
 
 template <bool BF16, int D, bool CAUSAL, bool VARLEN>
@@ -623,8 +636,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 s0 = mfma32<BF16>(qa[i], kf[i], s0);
+                FA_PIN_A(s0);
                 qb[i] = rows(Qb, 1, i);
                 d0 = mfma32<BF16>(ga[i], vf[i], d0);
+                FA_PIN_A(d0);
                 gb[i] = rows(Gb, 1, i);
                 fence();
             }
@@ -659,8 +674,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     #pragma unroll
                 for (int db = 0; db < ND; ++db) {
                     dvacc[db] = mfma32<BF16>(tg[db], pp[0], dvacc[db]);
+                    FA_PIN_A(dvacc[db]);
                     ug[db] = tr_operand<D>(g0r + 16 * ROWB, of, db);
                     dkacc[db] = mfma32<BF16>(tq[db], ss[0], dkacc[db]);
+                    FA_PIN_A(dkacc[db]);
                     uq[db] = tr_operand<D>(q0r + 16 * ROWB, of, db);
                     quarter(db);
                     fence();
@@ -668,7 +685,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     #pragma unroll
                 for (int db = 0; db < ND; ++db) {
                     dvacc[db] = mfma32<BF16>(ug[db], pp[1], dvacc[db]);
+                    FA_PIN_A(dvacc[db]);
                     dkacc[db] = mfma32<BF16>(uq[db], ss[1], dkacc[db]);
+                    FA_PIN_A(dkacc[db]);
                     quarter(ND + db);
                     fence();
                 }
