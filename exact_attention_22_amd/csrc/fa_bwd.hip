@@ -644,32 +644,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 fence();
             }
             // S and dP of rows 32..63 beside the element-wise work of rows 0..31
+            // (and the first transposed operands of rows 0..31's gradient products read
+            // beside them, so that those products start without waiting)
             u32x4 pb[2], sb[2], pb1[2], sb1[2];
+            u32x4 tg0[ND], tq0[ND], tg1[ND], tq1[ND];
     #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 s1 = mfma32<BF16>(qb[i], kf[i], s1);
                 d1 = mfma32<BF16>(gb[i], vf[i], d1);
+                if (i < ND) {
+                    tg0[i] = tr_operand<D>(Gb, of, i);
+                    tq0[i] = tr_operand<D>(Qb, of, i);
+                }
             }
             dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
             fence();
             // dV^T += dO^T P and dK^T += Q^T dS over one 32-row block: the transposed
-            // operands of its first 16 rows up front, those of the next 16 beside the
-            // first products; `before` runs first, and the four quarters of `beside`
-            // run spread over the products
-            auto accum = [&](int kb, const u32x4 (&pp)[2], const u32x4 (&ss)[2], auto&& before, auto&& beside) {
+            // operands of its first 16 rows (tg, tq) already read, those of the next 16
+            // beside the first products; `before` runs first, the four quarters of
+            // `beside` run spread over the products, and `next(db)` reads operands
+            // for what follows beside the second half's products
+            auto accum = [&](int kb, const u32x4 (&pp)[2], const u32x4 (&ss)[2], const u32x4 (&tg)[ND],
+                             const u32x4 (&tq)[ND], auto&& before, auto&& beside, auto&& next) {
                 const unsigned char* q0r = Qb + (32 * kb) * ROWB;
                 const unsigned char* g0r = Gb + (32 * kb) * ROWB;
                 before();
-                u32x4 tg[ND], tq[ND], ug[ND], uq[ND];
+                u32x4 ug[ND], uq[ND];
                 // the 2 ND product pairs carry the four quarters of `beside` evenly
                 auto quarter = [&](int u) {
                     if (((u + 1) * 4) % (2 * ND) == 0) beside((u + 1) * 4 / (2 * ND) - 1);
                 };
-    #pragma unroll
-                for (int db = 0; db < ND; ++db) {
-                    tg[db] = tr_operand<D>(g0r, of, db);
-                    tq[db] = tr_operand<D>(q0r, of, db);
-                }
                 fence();
     #pragma unroll
                 for (int db = 0; db < ND; ++db) {
@@ -689,6 +693,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                     dkacc[db] = mfma32<BF16>(uq[db], ss[1], dkacc[db]);
                     FA_PIN_A(dkacc[db]);
                     quarter(ND + db);
+                    next(db);
                     fence();
                 }
             };
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             // (its LSE and D values are read before the transposed operands: LDS reads
             // complete in order, so a later read would wait for all of those)
             f32x4 l1[4], dd1[4];
-            accum(0, pb, sb, [&] {
+            accum(0, pb, sb, tg0, tq0, [&] {
     #pragma unroll
                 for (int qtr = 0; qtr < 4; ++qtr) {
                     const int o = 32 + 8 * h + 16 * (qtr >> 1) + 4 * (qtr & 1);
@@ -707,8 +712,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             }, [&](int qtr) {
                 const int p = qtr >> 1, e0 = 4 * (qtr & 1);
                 dkdv_probs4<BF16, MASK>(s1, d1, l1[qtr], dd1[qtr], a.c, lim - 32, p, e0, pb1[p], sb1[p]);
+            }, [&](int db) {
+                tg1[db] = tr_operand<D>(Gb + 32 * ROWB, of, db);
+                tq1[db] = tr_operand<D>(Qb + 32 * ROWB, of, db);
             });
-            accum(1, pb1, sb1, [] {}, [](int) {});
+            accum(1, pb1, sb1, tg1, tq1, [] {}, [](int) {}, [](int) {});
         };
 
         // Query tiles upward from the diagonal, for each query head of the group in
