@@ -648,17 +648,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             // beside them, so that those products start without waiting)
             u32x4 pb[2], sb[2], pb1[2], sb1[2];
             u32x4 tg0[ND], tq0[ND], tg1[ND], tq1[ND];
+            if constexpr (D == 128) {
+                // the element-wise work of rows 0..31 in quarters between the score
+                // products of rows 32..63 (at d = 64 the extra registers would cost
+                // the second wavefront per SIMD)
+                f32x4 l0[4], dd0[4];
     #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                s1 = mfma32<BF16>(qb[i], kf[i], s1);
-                d1 = mfma32<BF16>(gb[i], vf[i], d1);
-                if (i < ND) {
-                    tg0[i] = tr_operand<D>(Gb, of, i);
-                    tq0[i] = tr_operand<D>(Qb, of, i);
+                for (int qtr = 0; qtr < 4; ++qtr) {
+                    const int o = 8 * h + 16 * (qtr >> 1) + 4 * (qtr & 1);
+                    l0[qtr] = *(const f32x4*)(Ls + o);
+                    dd0[qtr] = *(const f32x4*)(Ds + o);
                 }
+    #pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    s1 = mfma32<BF16>(qb[i], kf[i], s1);
+                    FA_PIN_A(s1);
+                    d1 = mfma32<BF16>(gb[i], vf[i], d1);
+                    FA_PIN_A(d1);
+                    if (i < ND) {
+                        tg0[i] = tr_operand<D>(Gb, of, i);
+                        tq0[i] = tr_operand<D>(Qb, of, i);
+                    }
+                    if (i % (NS / 4) == NS / 4 - 1) {
+                        const int qtr = i / (NS / 4), p = qtr >> 1, e0 = 4 * (qtr & 1);
+                        dkdv_probs4<BF16, MASK>(s0, d0, l0[qtr], dd0[qtr], a.c, lim, p, e0, pb[p], sb[p]);
+                    }
+                    fence();
+                }
+            } else {
+    #pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    s1 = mfma32<BF16>(qb[i], kf[i], s1);
+                    d1 = mfma32<BF16>(gb[i], vf[i], d1);
+                    if (i < ND) {
+                        tg0[i] = tr_operand<D>(Gb, of, i);
+                        tq0[i] = tr_operand<D>(Qb, of, i);
+                    }
+                }
+                dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
+                fence();
             }
-            dkdv_probs<BF16, MASK>(s0, d0, Ls, Ds, 8 * h, a.c, lim, pb, sb);
-            fence();
             // dV^T += dO^T P and dK^T += Q^T dS over one 32-row block: the transposed
             // operands of its first 16 rows (tg, tq) already read, those of the next 16
             // beside the first products; `before` runs first, the four quarters of
