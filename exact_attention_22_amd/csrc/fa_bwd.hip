@@ -28,10 +28,12 @@
 //     dS feed dV^T += dO^T P and dK^T += Q^T dS directly.  LSE (in base 2) and
 //     D of the tile's query rows sit in LDS next to the Q and dO tiles.  At one
 //     wave per SIMD no other wave hides a wave's LDS latency, so the instruction
-//     order is fixed by scheduling fences: operand reads (above all the
-//     transposed ones) run 8 to 16 reads ahead of their products, the first
-//     block's element-wise work runs beside the second block's scores, and the
-//     second block's beside the first block's gradient products.
+//     order is fixed by scheduling fences (which order memory operations) and
+//     empty asm statements on the products' accumulators (which keep the pure
+//     arithmetic between them): operand reads (above all the transposed ones)
+//     run 8 to 16 reads ahead of their products, the first block's element-wise
+//     work runs beside the second block's scores, and the second block's beside
+//     the first block's gradient products.
 //   * Rows past the end of Q read as zeros (so they add nothing to dK, dV), and
 //     keys past the end of K only reach their own, unstored, dK/dV columns; the
 //     dK/dV kernel therefore only applies the causal condition, as a select per
