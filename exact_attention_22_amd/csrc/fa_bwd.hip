@@ -650,6 +650,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             // beside them, so that those products start without waiting)
             u32x4 pb[2], sb[2], pb1[2], sb1[2];
             u32x4 tg0[ND], tq0[ND], tg1[ND], tq1[ND];
+            f32x4 l1[4], dd1[4];
+            // LSE and D of rows 32..63 (read before the transposed operands that follow
+            // them: LDS reads complete in order, so a later read would wait for those)
+            auto read_ld1 = [&](int qtr) {
+                const int o = 32 + 8 * h + 16 * (qtr >> 1) + 4 * (qtr & 1);
+                l1[qtr] = *(const f32x4*)(Ls + o);
+                dd1[qtr] = *(const f32x4*)(Ds + o);
+            };
             if constexpr (D == 128) {
                 // the element-wise work of rows 0..31 in quarters between the score
                 // products of rows 32..63 (at d = 64 the extra registers would cost
@@ -670,6 +678,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                     if (i < ND) {
                         tg0[i] = tr_operand<D>(Gb, of, i);
                         tq0[i] = tr_operand<D>(Qb, of, i);
+                    } else if (i < ND + 4) {
+                        read_ld1(i - ND);
                     }
                     if (i % (NS / 4) == NS / 4 - 1) {
                         const int qtr = i / (NS / 4), p = qtr >> 1, e0 = 4 * (qtr & 1);
@@ -729,17 +739,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 }
             };
             // the element-wise work of rows 32..63, a quarter beside every four products
-            // of rows 0..31
-            // (its LSE and D values are read before the transposed operands: LDS reads
-            // complete in order, so a later read would wait for all of those)
-            f32x4 l1[4], dd1[4];
+            // of rows 0..31 (at d = 128 its LSE and D values were read beside the
+            // score products)
             accum(0, pb, sb, tg0, tq0, [&] {
+                if constexpr (D != 128)
     #pragma unroll
-                for (int qtr = 0; qtr < 4; ++qtr) {
-                    const int o = 32 + 8 * h + 16 * (qtr >> 1) + 4 * (qtr & 1);
-                    l1[qtr] = *(const f32x4*)(Ls + o);
-                    dd1[qtr] = *(const f32x4*)(Ds + o);
-                }
+                    for (int qtr = 0; qtr < 4; ++qtr) read_ld1(qtr);
             }, [&](int qtr) {
                 const int p = qtr >> 1, e0 = 4 * (qtr & 1);
                 dkdv_probs4<BF16, MASK>(s1, d1, l1[qtr], dd1[qtr], a.c, lim - 32, p, e0, pb1[p], sb1[p]);
